@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the WavePrune hot path on one MI355X; prints one JSON line.
+
+A step is one pass of the whole path over resident synthetic inputs:
+  RoPE of Q and K (32K prefill) -> WavePrune prefill (32K, 32/8 heads,
+  d_h 128, theta 1e6, G 16) -> RoPE of the 16 decode queries -> WavePrune
+  decode (16 sequences x 32K cached tokens, 32/8 heads).
+The in-house dense baseline (same kernels, every group full) is timed the
+same way right after, for the speedups.  Kernel times come from HIP events
+recorded on the stream the library launches on.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("prefill dense-equiv TFLOPS + decode KV GB/s at 32K, d_h=128; "
+          "speedup vs own dense")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# work accounting (per launch)
+# ---------------------------------------------------------------------------
+def prefill_flops(n, Hq, B, d_h, G, cut):
+    """Dense-equivalent, algorithmic (per causal pair: 2*G per kept group +
+    2*d_h for P.V) and executed (per visited 32x32 tile: 2*32*32*G per
+    non-skipped group + 2*32*32*d_h) FLOPs."""
+    import rope_positional_encoding_amd as W
+    dense = 4.0 * d_h * n * (n + 1) / 2.0
+    alg = 2.0 * d_h * n * (n + 1) / 2.0
+    for D in cut:
+        m = min(int(D), n - 1)
+        # causal pairs with distance 0..m: sum_{t=0..m} (n - t)
+        alg += 2.0 * G * ((m + 1) * n - m * (m + 1) / 2.0)
+    cnt = W.prefill_tile_counts(n, d_h, G, cut)
+    ng = d_h // G
+    BM, BN = W.prefill_tiling(d_h, G)
+    tile = 2.0 * BM * BN
+    visited = cnt[3 * ng]
+    exe = visited * tile * d_h
+    for g in range(ng):
+        exe += (cnt[3 * g + 1] + cnt[3 * g + 2]) * tile * G
+    k = B * Hq
+    return dense * k, alg * k, exe * k
+
+
+def decode_bytes(L, q_pos, Hkv, Hq, B, d_h, G, cut):
+    """Dense KV bytes, algorithmic bytes (kept K groups + all V + q/o) and
+    the bytes of the K/V reads the kernel issues (per 32-key block)."""
+    import rope_positional_encoding_amd as W
+    dense = 2.0 * 2 * L * d_h
+    kept_k = 0.0
+    for D in cut:
+        # keys j with q_pos - j <= D, j in [0, L)
+        lo = max(0, q_pos - int(D))
+        kept_k += 2.0 * G * max(0, L - lo)
+    alg = kept_k + 2.0 * L * d_h
+    cnt = W.decode_tile_counts(q_pos, L, d_h, G, cut)
+    ng = d_h // G
+    BN = W.decode_tiling(d_h, G)
+    issued = 0.0
+    for g in range(ng):
+        issued += (cnt[3 * g + 1] + cnt[3 * g + 2]) * BN * 2.0 * G
+    issued += 2.0 * L * d_h
+    k = B * Hkv
+    qo = 2.0 * 2 * B * Hq * d_h
+    return dense * k, alg * k + qo, issued * k + qo
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512):
+    """The CPU oracle (as it stands) on seeded uniform query rows of the same
+    32K prefill (the rotated inputs the GPU consumed), single BLAS thread;
+    scaled to dense-equivalent TFLOP/s."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, n, size=max_rows)
+    q64 = f64(qr[0, torch.from_numpy(rows).to(qr.device)])
+    k64 = f64(kr[0])
+    v64 = f64(v[0])
+    cut = O.group_cutoffs(theta, d_h, G)
+    dc = O.dim_cutoffs_grouped(cut, G)
+    done = 0
+    flops = 0.0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while done < max_rows and (time.perf_counter() - t0 < seconds or done < 4):
+            i = int(rows[done])
+            O.prefill(q64[done:done + 1], k64, v64, dc, rows=[i], q_is_rows=True)
+            flops += 4.0 * d_h * Hq * (i + 1)
+            done += 1
+        dt = time.perf_counter() - t0
+    done_rows = rows[:done]
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s (prefill, dense-equivalent)",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d seeded uniform query rows x %d heads of the 32K prefill "
+                  "(grouped rule, float64 numpy, 1 BLAS thread), %.1f s" % (len(done_rows), Hq, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the path needs no "
+              "collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_positional_encoding_amd as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    # prefill32k_g16 and decode32k shapes
+    n, Hq, Hkv, d, G, theta = 32768, 32, 8, 128, 16, 1e6
+    Bd, L, q_pos = 16, 32768, 32768
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    log("bench: allocating inputs")
+    q_raw = randn(1, n, Hq, d)
+    k_raw = randn(1, n, Hkv, d)
+    v = randn(1, n, Hkv, d)
+    qr = torch.empty_like(q_raw)
+    kr = torch.empty_like(k_raw)
+    o = torch.empty_like(q_raw)
+    dq_raw = randn(Bd, 1, Hq, d)
+    dqr = torch.empty_like(dq_raw)
+    kc = W.rope_apply(randn(Bd, L, Hkv, d), theta)     # the cache holds rotated keys
+    vc = randn(Bd, L, Hkv, d)
+    od = torch.empty(Bd, Hq, d, dtype=torch.bfloat16, device=dev)
+    cl = torch.full((Bd,), L, dtype=torch.int32, device=dev)
+    qp = torch.full((Bd,), q_pos, dtype=torch.int32, device=dev)
+    qp64 = torch.full((Bd,), q_pos, dtype=torch.int64, device=dev)
+    ws = torch.empty(W.decode_workspace_size(Bd, L, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    cut = W.group_cutoffs(theta, d, G)
+    torch.cuda.synchronize()
+
+    names = ["rope_q", "rope_k", "prefill", "rope_dq", "decode"]
+
+    def step(ev, dense=False):
+        s = torch.cuda.current_stream()
+        e = ev
+        e[0].record(s)
+        W.rope_apply(q_raw, theta, out=qr)
+        e[1].record(s)
+        W.rope_apply(k_raw, theta, out=kr)
+        e[2].record(s)
+        W.prefill(qr, kr, v, None if dense else cut, G, dense=dense, out=o)
+        e[3].record(s)
+        W.rope_apply(dq_raw, theta, pos_start=qp64, out=dqr)
+        e[4].record(s)
+        W.decode(dqr[:, 0], kc, vc, cl, qp, None if dense else cut, G, dense=dense,
+                 workspace=ws, out=od)
+        e[5].record(s)
+
+    def run(dense):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        warm = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for _ in range(args.warmup):
+            step(warm, dense)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step(evs[k], dense)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {nm: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]
+               for i, nm in enumerate(names)}
+        total = sum(evs[k][0].elapsed_time(evs[k][5]) for k in range(args.steps))
+        return per, total / args.steps, wall
+
+    log("bench: WavePrune steps")
+    per, ms_step, wall = run(False)
+    log("bench: dense baseline steps")
+    per_d, ms_step_d, _ = (None, None, None) if args.no_dense else run(True)
+
+    med = {k: statistics.median(v_) for k, v_ in per.items()}
+    avg = {k: sum(v_) / len(v_) for k, v_ in per.items()}
+    dense_f, alg_f, exe_f = prefill_flops(n, Hq, 1, d, G, cut)
+    kv_dense, dec_alg, dec_issued = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G, cut)
+    rope_bytes = 2 * 2.0 * (q_raw.numel() + k_raw.numel())
+
+    out = {
+        "metric": METRIC,
+        "value": round(dense_f / (med["prefill"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill32k_g16 + decode32k",
+                   "prefill": {"B": 1, "n": n, "Hq": Hq, "Hkv": Hkv, "d_h": d, "theta": theta, "G": G},
+                   "decode": {"B": Bd, "cache_len": L, "q_pos": q_pos, "Hq": Hq, "Hkv": Hkv,
+                              "d_h": d, "theta": theta, "G": G}},
+        "prefill": {
+            "ms_median": round(med["prefill"], 4), "ms_min": round(min(per["prefill"]), 4),
+            "ms_max": round(max(per["prefill"]), 4),
+            "dense_equiv_tflops": round(dense_f / (med["prefill"] * 1e-3) / 1e12, 2),
+            "algorithmic_tflops": round(alg_f / (med["prefill"] * 1e-3) / 1e12, 2),
+            "executed_tflops": round(exe_f / (med["prefill"] * 1e-3) / 1e12, 2),
+            "algorithmic_fraction_of_dense": round(alg_f / dense_f, 4),
+            "executed_fraction_of_dense": round(exe_f / dense_f, 4),
+        },
+        "decode": {
+            "ms_median": round(med["decode"], 4), "ms_min": round(min(per["decode"]), 4),
+            "kv_gbs_dense_equiv": round(kv_dense / (med["decode"] * 1e-3) / 1e9, 1),
+            "algorithmic_gbs": round(dec_alg / (med["decode"] * 1e-3) / 1e9, 1),
+            "issued_gbs": round(dec_issued / (med["decode"] * 1e-3) / 1e9, 1),
+            "algorithmic_fraction_of_dense": round(dec_alg / kv_dense, 4),
+        },
+        "rope": {"ms_q": round(med["rope_q"], 4), "ms_k": round(med["rope_k"], 4),
+                 "gbs": round(rope_bytes / ((med["rope_q"] + med["rope_k"]) * 1e-3) / 1e9, 1)},
+    }
+    if per_d is not None:
+        med_d = {k: statistics.median(v_) for k, v_ in per_d.items()}
+        out["prefill"]["dense_ms_median"] = round(med_d["prefill"], 4)
+        out["prefill"]["dense_tflops"] = round(dense_f / (med_d["prefill"] * 1e-3) / 1e12, 2)
+        out["prefill"]["speedup_vs_dense"] = round(med_d["prefill"] / med["prefill"], 4)
+        out["decode"]["dense_ms_median"] = round(med_d["decode"], 4)
+        out["decode"]["dense_kv_gbs"] = round(kv_dense / (med_d["decode"] * 1e-3) / 1e9, 1)
+        out["decode"]["speedup_vs_dense"] = round(med_d["decode"] / med["decode"], 4)
+    # roofline of the dominant kernel (prefill): algorithmic FLOPs per launch
+    # over the average launch duration measured with events on its stream
+    ach = alg_f / (avg["prefill"] * 1e-3) / 1e12
+    out["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                       "kernel": "prefill_kernel<128,16>", "avg_ms": round(avg["prefill"], 4)}
+    ach_d = dec_alg / (avg["decode"] * 1e-3) / 1e9
+    out["roofline_decode"] = {"bound": "hbm", "achieved": round(ach_d, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4), "traffic": None,
+                              "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
+                              "avg_ms": round(avg["decode"], 4)}
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

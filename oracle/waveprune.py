@@ -138,15 +138,16 @@ def softmax_av(L: np.ndarray, v: np.ndarray):
 
 
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, dim_cut: np.ndarray,
-            rows=None, positions=None, return_lse: bool = False):
+            rows=None, positions=None, return_lse: bool = False, q_is_rows: bool = False):
     """Causal WavePrune attention for one sequence.
 
     q [n, Hq, d_h], k/v [n, Hkv, d_h] (q and k already rotated); query row i
     sees keys j <= i; dist = positions[i] - positions[j] (default positions
-    0..n-1, so dist = i - j).  Returns O [len(rows), Hq, d_h] (and LSE
-    [len(rows), Hq]).
+    0..n-1, so dist = i - j).  With q_is_rows, q holds only the listed rows,
+    in order.  Returns O [len(rows), Hq, d_h] (and LSE [len(rows), Hq]).
     """
-    n, Hq, d_h = q.shape
+    n = k.shape[0]
+    Hq, d_h = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
     r = Hq // Hkv
     pos = np.arange(n, dtype=np.int64) if positions is None else np.asarray(positions, np.int64)
@@ -157,7 +158,7 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, dim_cut: np.ndarray,
         dist = pos[i] - pos[: i + 1]
         for kv in range(Hkv):
             hs = slice(kv * r, (kv + 1) * r)
-            L = logits(q[i, hs, :], k[: i + 1, kv, :], dist, dim_cut)
+            L = logits(q[idx if q_is_rows else i, hs, :], k[: i + 1, kv, :], dist, dim_cut)
             out[idx, hs], lse[idx, hs] = softmax_av(L, v[: i + 1, kv, :])
     return (out, lse) if return_lse else out
 

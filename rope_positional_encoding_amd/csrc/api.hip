@@ -1,0 +1,354 @@
+// libwaveprune C ABI: argument validation, the cutoff table, the host tile
+// classifier and kernel dispatch.  See include/waveprune.h for the contract.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/waveprune.h"
+#include "wp_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+wp_status fail(wp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+wp_status ok() {
+  g_last_error[0] = '\0';
+  return WP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_shape(int32_t d_h, int32_t G) {
+  return (d_h == 64 || d_h == 128) && (G == 16 || G == 32);
+}
+
+// Cutoffs must be a non-decreasing, non-negative table: the tile classes
+// then form a skip prefix / partial middle / full suffix.
+wp_status check_cutoffs(const int32_t* cut, int32_t ng) {
+  for (int g = 0; g < ng; ++g) {
+    if (cut[g] < 0) return fail(WP_ERR_ARG, "cutoffs[%d] = %d is negative", g, cut[g]);
+    if (g > 0 && cut[g] < cut[g - 1])
+      return fail(WP_ERR_ARG, "cutoffs must be non-decreasing (cutoffs[%d] = %d < cutoffs[%d] = %d)",
+                  g, cut[g], g - 1, cut[g - 1]);
+  }
+  return WP_OK;
+}
+
+wp_status check_strides(const int64_t* st, int count) {
+  for (int i = 0; i < count; ++i) {
+    if (st[i] < 0) return fail(WP_ERR_SHAPE, "stride %d is negative (%lld)", i, (long long)st[i]);
+    if (st[i] % 8) return fail(WP_ERR_ALIGN, "stride %d = %lld is not a multiple of 8 elements",
+                               i, (long long)st[i]);
+  }
+  return WP_OK;
+}
+
+// Classes of one tile with causal distances [lD, rD]: skip groups
+// [0, splitL), partial [splitL, splitR), full [splitR, ng).
+inline void add_tile(const int32_t* cut, int ng, int64_t lD, int64_t rD, int64_t* counts) {
+  int sL = 0, sR = 0;
+  for (int g = 0; g < ng; ++g) {
+    sL += cut[g] < lD;
+    sR += cut[g] < rD;
+  }
+  for (int g = 0; g < ng; ++g) counts[3 * g + (g < sL ? 0 : (g < sR ? 1 : 2))] += 1;
+  counts[3 * ng] += 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wp_version(void) { return "0.1.0"; }
+
+const char* wp_last_error(void) { return g_last_error; }
+
+const char* wp_status_string(wp_status s) {
+  switch (s) {
+    case WP_OK: return "ok";
+    case WP_ERR_NULL: return "null pointer";
+    case WP_ERR_SHAPE: return "bad shape";
+    case WP_ERR_UNSUPPORTED: return "unsupported head dim or group size";
+    case WP_ERR_ALIGN: return "misaligned pointer or stride";
+    case WP_ERR_WORKSPACE: return "workspace too small";
+    case WP_ERR_ARG: return "bad argument";
+    case WP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+wp_status wp_group_cutoffs(double theta, int32_t d_h, int32_t G, double pos_scale, int32_t* out,
+                           int32_t out_len) {
+  if (!out) return fail(WP_ERR_NULL, "out is NULL");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(WP_ERR_ARG, "theta must be finite and > 0");
+  if (!(pos_scale > 0.0) || !isfinite(pos_scale))
+    return fail(WP_ERR_ARG, "pos_scale must be finite and > 0");
+  if (d_h <= 0 || d_h % 2) return fail(WP_ERR_SHAPE, "d_h = %d must be positive and even", d_h);
+  if (G <= 0 || G % 2 || d_h % G) return fail(WP_ERR_SHAPE, "G = %d must be even and divide d_h", G);
+  if (out_len != d_h / G) return fail(WP_ERR_SHAPE, "out_len = %d, expected d_h/G = %d", out_len, d_h / G);
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int g = 0; g < out_len; ++g) {
+    double best = -1.0;
+    // channels of dims [gG, (g+1)G) are c = gG/2 .. (g+1)G/2 - 1
+    for (int c = g * G / 2; c < (g + 1) * G / 2; ++c) {
+      const double f = pow(theta, -2.0 * (double)c / (double)d_h) / pos_scale;   // scaled frequency
+      const double w = floor(two_pi / f);                                        // kept distances
+      if (w > best) best = w;
+    }
+    out[g] = (best >= 2147483647.0 || !isfinite(best)) ? WP_NEVER_PRUNE : (int32_t)best;
+  }
+  return ok();
+}
+
+wp_status wp_prefill_tiling(int32_t d_h, int32_t G, int32_t* BM, int32_t* BN) {
+  if (!BM || !BN) return fail(WP_ERR_NULL, "BM/BN is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  *BM = wp::kPrefillBM;
+  *BN = wp::kPrefillBN;
+  return ok();
+}
+
+wp_status wp_decode_tiling(int32_t d_h, int32_t G, int32_t* BN) {
+  if (!BN) return fail(WP_ERR_NULL, "BN is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  *BN = wp::kDecodeBN;
+  return ok();
+}
+
+wp_status wp_prefill_tile_counts(int32_t n, int32_t d_h, int32_t G, const int32_t* cutoffs,
+                                 int64_t* counts) {
+  if (!cutoffs || !counts) return fail(WP_ERR_NULL, "cutoffs/counts is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (n < 1) return fail(WP_ERR_SHAPE, "n = %d must be >= 1", n);
+  const int ng = d_h / G;
+  if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+  memset(counts, 0, sizeof(int64_t) * (3 * ng + 1));
+  const int BM = wp::kPrefillBM, BN = wp::kPrefillBN;
+  for (int64_t i0 = 0; i0 < n; i0 += BM) {
+    const int64_t i1 = (i0 + BM < n ? i0 + BM : n) - 1;
+    for (int64_t j0 = 0; j0 <= i1; j0 += BN) {
+      const int64_t j1 = (j0 + BN < n ? j0 + BN : n) - 1;
+      const int64_t lD = i0 - j1 > 0 ? i0 - j1 : 0;
+      add_tile(cutoffs, ng, lD, i1 - j0, counts);
+    }
+  }
+  return ok();
+}
+
+wp_status wp_decode_tile_counts(int32_t q_pos, int32_t cache_len, int32_t d_h, int32_t G,
+                                const int32_t* cutoffs, int64_t* counts) {
+  if (!cutoffs || !counts) return fail(WP_ERR_NULL, "cutoffs/counts is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (cache_len < 0) return fail(WP_ERR_SHAPE, "cache_len = %d must be >= 0", cache_len);
+  if (cache_len > 0 && q_pos < cache_len - 1)
+    return fail(WP_ERR_ARG, "q_pos = %d must be >= cache_len - 1 = %d", q_pos, cache_len - 1);
+  const int ng = d_h / G;
+  if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+  memset(counts, 0, sizeof(int64_t) * (3 * ng + 1));
+  const int BN = wp::kDecodeBN;
+  for (int64_t j0 = 0; j0 < cache_len; j0 += BN) {
+    const int64_t j1 = (j0 + BN < cache_len ? j0 + BN : cache_len) - 1;
+    add_tile(cutoffs, ng, (int64_t)q_pos - j1, (int64_t)q_pos - j0, counts);
+  }
+  return ok();
+}
+
+wp_status wp_rope_apply(const void* x, int32_t x_dtype, void* y, int32_t B, int32_t n, int32_t H,
+                        int32_t d_h, const int64_t x_strides[3], const int64_t y_strides[3],
+                        const int64_t* pos_start, double theta, double pos_scale, void* stream) {
+  if (!x || !y || !x_strides || !y_strides) return fail(WP_ERR_NULL, "x, y or strides is NULL");
+  if (x_dtype != WP_DTYPE_BF16 && x_dtype != WP_DTYPE_F32)
+    return fail(WP_ERR_ARG, "x_dtype = %d must be WP_DTYPE_BF16 or WP_DTYPE_F32", x_dtype);
+  if (d_h != 64 && d_h != 128) return fail(WP_ERR_UNSUPPORTED, "d_h = %d unsupported", d_h);
+  if (B < 1 || n < 1 || H < 1) return fail(WP_ERR_SHAPE, "B, n, H must be >= 1");
+  if ((int64_t)B * n > 2147483647LL) return fail(WP_ERR_SHAPE, "B*n exceeds 2^31-1");
+  if (!(theta > 0.0) || !isfinite(theta)) return fail(WP_ERR_ARG, "theta must be finite and > 0");
+  if (!(pos_scale > 0.0) || !isfinite(pos_scale))
+    return fail(WP_ERR_ARG, "pos_scale must be finite and > 0");
+  if (!aligned16(x) || !aligned16(y)) return fail(WP_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if (wp_status s = check_strides(x_strides, 3)) return s;
+  if (wp_status s = check_strides(y_strides, 3)) return s;
+  if (x == y) {
+    if (x_dtype != WP_DTYPE_BF16 || memcmp(x_strides, y_strides, 3 * sizeof(int64_t)) != 0)
+      return fail(WP_ERR_ARG, "in-place RoPE needs a bf16 input with identical strides");
+  }
+  if (pos_start && (reinterpret_cast<uintptr_t>(pos_start) & 7u))
+    return fail(WP_ERR_ALIGN, "pos_start must be 8-byte aligned");
+  wp::RopeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.y = y;
+  a.pos_start = pos_start;
+  a.xs_b = x_strides[0]; a.xs_t = x_strides[1]; a.xs_h = x_strides[2];
+  a.ys_b = y_strides[0]; a.ys_t = y_strides[1]; a.ys_h = y_strides[2];
+  a.B = B; a.n = n; a.H = H; a.d_h = d_h;
+  a.x_f32 = (x_dtype == WP_DTYPE_F32);
+  for (int c = 0; c < d_h / 2; ++c)
+    a.inv_freq[c] = pow(theta, -2.0 * (double)c / (double)d_h) / pos_scale;
+  hipError_t e = wp::launch_rope(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "rope launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                     int32_t n, int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[12],
+                     const int32_t* cutoffs, int32_t G, uint32_t flags, int64_t* counters,
+                     void* stream) {
+  if (!q || !k || !v || !o || !strides) return fail(WP_ERR_NULL, "q, k, v, o or strides is NULL");
+  if (flags & ~(WP_FLAG_DENSE | WP_FLAG_COUNT)) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
+  const bool dense = flags & WP_FLAG_DENSE;
+  const bool count = flags & WP_FLAG_COUNT;
+  if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
+  if (count && !counters) return fail(WP_ERR_NULL, "counters is NULL with WP_FLAG_COUNT");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (B < 1 || n < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, n, Hq, Hkv must be >= 1");
+  if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(WP_ERR_ALIGN, "q, k, v, o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WP_ERR_ALIGN, "lse misaligned");
+  if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
+    return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
+  if (wp_status s = check_strides(strides, 12)) return s;
+  const int ng = d_h / G;
+  wp::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  if (dense) {
+    for (int g = 0; g < wp::kMaxGroups; ++g) a.cut[g] = WP_NEVER_PRUNE;
+  } else {
+    if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+    for (int g = 0; g < ng; ++g) a.cut[g] = cutoffs[g];
+  }
+  a.q = static_cast<const wp::bf16*>(q);
+  a.k = static_cast<const wp::bf16*>(k);
+  a.v = static_cast<const wp::bf16*>(v);
+  a.o = static_cast<wp::bf16*>(o);
+  a.lse = lse;
+  a.counters = reinterpret_cast<unsigned long long*>(counters);
+  a.qs_b = strides[0]; a.qs_t = strides[1]; a.qs_h = strides[2];
+  a.ks_b = strides[3]; a.ks_t = strides[4]; a.ks_h = strides[5];
+  a.vs_b = strides[6]; a.vs_t = strides[7]; a.vs_h = strides[8];
+  a.os_b = strides[9]; a.os_t = strides[10]; a.os_h = strides[11];
+  a.B = B; a.n = n; a.Hq = Hq; a.Hkv = Hkv;
+  a.r = Hq / Hkv;
+  a.HPW = (a.r % 4 == 0) ? 4 : (a.r % 2 == 0 ? 2 : 1);
+  a.QSUB = 4 / a.HPW;
+  a.HG = a.r / a.HPW;
+  a.QB = 32 * a.QSUB;
+  a.nqb = (n + a.QB - 1) / a.QB;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
+  const long long blocks = (long long)B * Hkv * a.HG * a.nqb;
+  if (blocks > 2147483647LL) return fail(WP_ERR_SHAPE, "grid too large");
+  hipError_t e = wp::launch_prefill(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t wp_decode_num_splits(int32_t B, int32_t Lmax, int32_t Hkv) {
+  if (B < 1 || Hkv < 1 || Lmax < 1) return 1;
+  const long long units = (long long)B * Hkv;
+  long long s = (2048 + units - 1) / units;                 // about 2048 workgroups
+  const long long max_s = ((long long)Lmax + 127) / 128;    // at least 128 keys per split
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+namespace {
+// split geometry: split_len is a multiple of the decode key block
+void decode_geometry(int32_t B, int32_t Lmax, int32_t Hkv, int32_t num_splits, int* S, int* split_len) {
+  int s = num_splits > 0 ? num_splits : wp_decode_num_splits(B, Lmax, Hkv);
+  long long len = ((long long)Lmax + s - 1) / s;
+  len = ((len + wp::kDecodeBN - 1) / wp::kDecodeBN) * wp::kDecodeBN;
+  if (len < wp::kDecodeBN) len = wp::kDecodeBN;
+  *split_len = (int)len;
+  *S = (int)(((long long)Lmax + len - 1) / len);
+}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+size_t wp_decode_workspace_size(int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv, int32_t d_h,
+                                int32_t num_splits) {
+  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d_h < 1) return 0;
+  int S, len;
+  decode_geometry(B, Lmax, Hkv, num_splits, &S, &len);
+  const size_t rows = (size_t)B * Hq * S;
+  return align256(rows * d_h * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                    const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
+                    int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[10],
+                    const int32_t* cutoffs, int32_t G, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, uint32_t flags, int64_t* counters, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !cache_len || !q_pos || !strides || !workspace)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  if (flags & ~(WP_FLAG_DENSE | WP_FLAG_COUNT)) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
+  const bool dense = flags & WP_FLAG_DENSE;
+  const bool count = flags & WP_FLAG_COUNT;
+  if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
+  if (count && !counters) return fail(WP_ERR_NULL, "counters is NULL with WP_FLAG_COUNT");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, Lmax, Hq, Hkv must be >= 1");
+  if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(WP_ERR_UNSUPPORTED, "decode supports at most 16 query heads per kv head");
+  if (num_splits < 0) return fail(WP_ERR_ARG, "num_splits must be >= 0");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(WP_ERR_ALIGN, "q, k_cache, v_cache, o must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(WP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cache_len) & 3u) || (reinterpret_cast<uintptr_t>(q_pos) & 3u))
+    return fail(WP_ERR_ALIGN, "cache_len / q_pos misaligned");
+  if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
+    return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
+  if (wp_status s = check_strides(strides, 10)) return s;
+  const size_t need = wp_decode_workspace_size(B, Lmax, Hq, Hkv, d_h, num_splits);
+  if (workspace_bytes < need)
+    return fail(WP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  const int ng = d_h / G;
+  wp::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  if (dense) {
+    for (int g = 0; g < wp::kMaxGroups; ++g) a.cut[g] = WP_NEVER_PRUNE;
+  } else {
+    if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+    for (int g = 0; g < ng; ++g) a.cut[g] = cutoffs[g];
+  }
+  int S, split_len;
+  decode_geometry(B, Lmax, Hkv, num_splits, &S, &split_len);
+  const size_t rows = (size_t)B * Hq * S;
+  a.q = static_cast<const wp::bf16*>(q);
+  a.k = static_cast<const wp::bf16*>(k_cache);
+  a.v = static_cast<const wp::bf16*>(v_cache);
+  a.o = static_cast<wp::bf16*>(o);
+  a.cache_len = cache_len;
+  a.q_pos = q_pos;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * d_h * sizeof(float)));
+  a.counters = reinterpret_cast<unsigned long long*>(counters);
+  a.qs_b = strides[0]; a.qs_h = strides[1];
+  a.ks_b = strides[2]; a.ks_t = strides[3]; a.ks_h = strides[4];
+  a.vs_b = strides[5]; a.vs_t = strides[6]; a.vs_h = strides[7];
+  a.os_b = strides[8]; a.os_h = strides[9];
+  a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv;
+  a.r = Hq / Hkv;
+  a.S = S;
+  a.split_len = split_len;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
+  const long long blocks = (long long)B * Hkv * S;
+  if (blocks > 2147483647LL || (long long)B * Hq > 2147483647LL)
+    return fail(WP_ERR_SHAPE, "grid too large");
+  hipError_t e = wp::launch_decode(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,358 @@
+// WavePrune decode attention for gfx950: one new query token per sequence
+// against a KV cache, split over the keys, then merged.
+//
+// Rule: a head-dim group adds to the logit only while the query-key distance
+// is within its cutoff; the key stays in the softmax (WavePrune reading notes
+// on cc.laoqi.cc, section 2.1, Eq. (6); grouped cutoffs, section 2.3,
+// Eq. (8)).  In decode a skipped group's K columns are never read
+// (section 2.3 table: skip = less QK and no K-cache read for the group; the
+// system section 4.6 attributes the decode gain to these K reads).
+//
+// gfx950 design:
+//  * HBM-bound: the aim is to stream the kept K bytes and all V bytes once.
+//    A workgroup (4 waves) owns one (sequence, kv head, key split); each wave
+//    walks its own 32-key blocks of the split independently (no barriers in
+//    the loop) and keeps its own online-softmax state for the GQA heads.
+//  * QK on v_mfma_f32_16x16x32_bf16 with the keys as rows: each lane loads
+//    16 contiguous bytes of one key row straight from HBM into the MFMA A
+//    operand; the GQA heads (<= 16) are the B columns, held in registers.
+//    Lanes whose 8 dims belong to a skipped group issue no load.
+//  * P.V on the same MFMA as O^T = V^T P^T: the probabilities are already in
+//    the B layout; V is staged through a per-wave LDS tile written transposed
+//    (keys permuted to match), so the A operand is one 16-byte LDS read.
+//  * The 4 waves merge through LDS at the end; a second kernel merges the
+//    splits (log-sum-exp weighted), one wave per (sequence, query head).
+#include "wp_internal.h"
+
+namespace wp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+__device__ inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline unsigned int pack_bf16x2(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
+         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+// Position of key-quad kq (keys 4kq..4kq+3 of a 32-key block) inside the
+// transposed V tile.  Lane quarter q of the P.V MFMA owns keys
+// {4q..4q+3} (block rows of the first 16 keys) and {16+4q..16+4q+3}; they
+// are stored at positions [8q, 8q+8).
+__device__ inline int vt_pos32(int kq) { return kq < 4 ? 8 * kq : 8 * (kq - 4) + 4; }
+
+template <int D, int G, bool COUNT>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  constexpr int NP = D / 32;          // 32-dim MFMA steps of QK
+  constexpr int NG = D / G;           // groups
+  constexpr int ND = D / 16;          // 16-dim output blocks
+  constexpr int VS = 32 + 8;          // V^T row stride in LDS (elements)
+  constexpr int VITEMS = 8 * (D / 8) / 64;   // (key quad, chunk) items per lane
+  static_assert(VITEMS >= 1, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) bf16 sV[kWaves][D * VS];
+  __shared__ float sM[kWaves][16];
+  __shared__ float sL[kWaves][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15;     // MFMA column: GQA head (B/C) or row (A)
+  const int q4 = lane >> 4;      // lane quarter
+
+  int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  bid /= a.Hkv;
+  const int split = bid % a.S;
+  const int b = bid / a.S;
+
+  const int L = min(a.cache_len[b], a.Lmax);
+  const int qp = a.q_pos[b];
+  const int ks0 = split * a.split_len;
+  const int ks1 = min(L, ks0 + a.split_len);
+
+  // Q^T operand: column n16 = head kvh*r + n16 (zero beyond r), dims
+  // [32p + 8q4, 32p + 8q4 + 8) of step p.
+  u32x4 qr[NP];
+  {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bf16* qb = a.q + (int64_t)b * a.qs_b + (int64_t)(kvh * a.r + n16) * a.qs_h + q4 * 8;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      qr[p] = (n16 < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
+  }
+
+  const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+  const bf16* vbase = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
+  bf16* sv = sV[wave];
+
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x4 o[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  unsigned int cnt[NG][3];
+  unsigned int cnt_vis = 0;
+  if (COUNT) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
+  }
+  const float sl2 = a.scale_log2;
+
+  for (int jb = ks0 + 32 * wave; jb < ks1; jb += 32 * kWaves) {
+    const int jb1 = min(L, jb + 32) - 1;
+    const int lD = qp - jb1;
+    const int rD = qp - jb;
+    int sL = 0, sR = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      sL += a.cut[g] < lD;
+      sR += a.cut[g] < rD;
+    }
+    if (COUNT) {
+      ++cnt_vis;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        cnt[g][0] += (g < sL);
+        cnt[g][1] += (g >= sL && g < sR);
+        cnt[g][2] += (g >= sR);
+      }
+    }
+
+    // ---- issue every HBM load of this block: kept K columns, all of V ----
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 kr[2][NP];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j = jb + 16 * blk + n16;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int g = (32 * p + 8 * q4) / G;      // this lane's group in step p
+        kr[blk][p] = (j <= jb1 && g >= sL)
+                         ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * a.ks_t + 32 * p + 8 * q4)
+                         : zero;
+      }
+    }
+    u32x4 vr[VITEMS][4];
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int kq = lane & 7;
+      const int dc = (lane >> 3) + 8 * it;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jb + 4 * kq + e;
+        vr[it][e] = (j <= jb1) ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * a.vs_t + dc * 8)
+                               : zero;
+      }
+    }
+
+    // ---- S^T = K Q^T per 16-key block, group by group ----
+    f32x4 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int g_lo = (32 * p) / G;             // groups covered by step p
+        const int g_hi = (32 * p + 31) / G;
+        if (g_hi < sL) continue;                   // every lane skipped
+        const int g = (32 * p + 8 * q4) / G;
+        bool any_full = false;
+#pragma unroll
+        for (int gg = g_lo; gg <= g_hi; ++gg) any_full |= (gg >= sR);
+        if (any_full) {
+          const u32x4 op = (g >= sR) ? kr[blk][p] : zero;
+          s[blk] = mfma16(op, qr[p], s[blk]);
+        }
+#pragma unroll
+        for (int gg = g_lo; gg <= g_hi; ++gg) {
+          if (gg < sL || gg >= sR) continue;       // only partial groups
+          const u32x4 op = (g == gg) ? kr[blk][p] : zero;
+          const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
+          const int cg = a.cut[gg];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = jb + 16 * blk + 4 * q4 + r;
+            s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jb + 16 * blk + 4 * q4 + r;
+        if (j > jb1) s[blk][r] = -INFINITY;
+      }
+    }
+
+    // ---- V^T into this wave's LDS tile ----
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int kq = lane & 7;
+      const int dc = (lane >> 3) + 8 * it;
+      const int pos = vt_pos32(kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned int w0 = vr[it][0][e], w1 = vr[it][1][e], w2 = vr[it][2][e], w3 = vr[it][3][e];
+        u32x2 even, odd;
+        even[0] = (w0 & 0xffffu) | (w1 << 16);
+        even[1] = (w2 & 0xffffu) | (w3 << 16);
+        odd[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+        odd[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+        const int d = dc * 8 + 2 * e;
+        *reinterpret_cast<u32x2*>(&sv[d * VS + pos]) = even;
+        *reinterpret_cast<u32x2*>(&sv[(d + 1) * VS + pos]) = odd;
+      }
+    }
+
+    // ---- online softmax over this block (log2 domain) ----
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_i, mx * sl2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+    l_i *= alpha;
+    float e[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[4 * blk + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], sl2, -m_use));
+        l_i += e[4 * blk + r];
+      }
+    u32x4 pb;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) o[db] *= alpha;
+    m_i = m_new;
+
+    // the V^T tile was written by other lanes of this wave
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(&sv[(16 * db + n16) * VS + 8 * q4]);
+      o[db] = mfma16(va, pb, o[db]);
+    }
+    // the next block overwrites the tile only after these reads completed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
+  // ---- merge the 4 waves of this split through LDS ----
+  const float l_tot = l_i + __shfl_xor(l_i, 16);
+  const float l_all = l_tot + __shfl_xor(l_tot, 32);
+  if (q4 == 0) {
+    sM[wave][n16] = m_i;
+    sL[wave][n16] = l_all;
+  }
+  __syncthreads();   // every wave is done with its V^T tile: reuse LDS for O
+  float* sO = reinterpret_cast<float*>(&sV[0][0]);   // [kWaves][16][D]
+  static_assert(sizeof(float) * kWaves * 16 * D <= sizeof(bf16) * kWaves * D * VS, "LDS reuse");
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sO[(wave * 16 + n16) * D + 16 * db + 4 * q4 + r] = o[db][r];
+  __syncthreads();
+
+  const int r_heads = a.r;
+  for (int idx = tid; idx < r_heads * D; idx += kThreads) {
+    const int hd = idx / D;
+    const int d = idx - hd * D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sM[w][hd]);
+    float acc = 0.f, lsum = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(sM[w][hd] - mm);
+        acc += sc * sO[(w * 16 + hd) * D + d];
+        lsum += sc * sL[w][hd];
+      }
+    }
+    const int h = kvh * a.r + hd;
+    const int64_t pi = ((int64_t)b * a.Hq + h) * a.S + split;
+    a.part_o[pi * D + d] = acc;
+    if (d == 0) {
+      a.part_ml[2 * pi] = mm;
+      a.part_ml[2 * pi + 1] = lsum;
+    }
+  }
+
+  if (COUNT && lane == 0) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int c = 0; c < 3; ++c)
+        if (cnt[g][c]) atomicAdd(&a.counters[3 * g + c], (unsigned long long)cnt[g][c]);
+    if (cnt_vis) atomicAdd(&a.counters[3 * NG], (unsigned long long)cnt_vis);
+  }
+}
+
+// One wave per (sequence, query head): O = sum_s 2^(m_s - m*) o_s /
+// sum_s 2^(m_s - m*) l_s.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int lane = threadIdx.x;
+  const int64_t base = (int64_t)bh * a.S;
+  float mm = -INFINITY;
+  for (int s = 0; s < a.S; ++s) mm = fmaxf(mm, a.part_ml[2 * (base + s)]);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  if (mm != -INFINITY) {
+    for (int s = 0; s < a.S; ++s) {
+      const float ms = a.part_ml[2 * (base + s)];
+      const float sc = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mm);
+      lsum += sc * a.part_ml[2 * (base + s) + 1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += sc * a.part_o[(base + s) * D + lane + 64 * e];
+    }
+  }
+  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+  bf16* op = a.o + (int64_t)b * a.os_b + (int64_t)h * a.os_h;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[lane + 64 * e] = static_cast<__bf16>(acc[e] * inv);
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, bool count, hipStream_t s) {
+  const long long blocks = (long long)a.B * a.Hkv * a.S;
+  if (blocks <= 0) return hipSuccess;
+  if (count)
+    hipLaunchKernelGGL((decode_split_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s) {
+  if (d_h == 128 && G == 16) return launch_dg<128, 16>(a, count, s);
+  if (d_h == 128 && G == 32) return launch_dg<128, 32>(a, count, s);
+  if (d_h == 64 && G == 16) return launch_dg<64, 16>(a, count, s);
+  if (d_h == 64 && G == 32) return launch_dg<64, 32>(a, count, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wp

@@ -1,0 +1,87 @@
+// Internal declarations shared by the libwaveprune sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxGroups = 8;       // d_h / G for d_h <= 128, G >= 16
+constexpr int kMaxChannels = 64;    // d_h / 2 for d_h <= 128
+
+// Tile geometry shared by the kernels, the host classifier and the tiling
+// queries.  Prefill: a tile is 32 queries of one head x 32 keys (one
+// 32x32 MFMA output block); decode: a key block of 32 keys.
+constexpr int kPrefillBM = 32;
+constexpr int kPrefillBN = 32;
+constexpr int kDecodeBN = 32;
+
+struct RopeArgs {
+  const void* x;
+  void* y;
+  const int64_t* pos_start;
+  int64_t xs_b, xs_t, xs_h;
+  int64_t ys_b, ys_t, ys_h;
+  int B, n, H, d_h;
+  int x_f32;
+  int rows_per_block;
+  double inv_freq[kMaxChannels];   // theta^(-2c/d_h) / pos_scale, float64
+};
+
+struct PrefillArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  unsigned long long* counters;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int B, n, Hq, Hkv;
+  int r;        // Hq / Hkv
+  int HPW;      // query heads per workgroup
+  int QSUB;     // 32-query sub-blocks per workgroup (4 / HPW)
+  int HG;       // head groups per kv head (r / HPW)
+  int QB;       // queries per workgroup (32 * QSUB)
+  int nqb;      // query blocks of QB
+  float scale_log2;   // log2(e) / sqrt(d_h)
+  int cut[kMaxGroups];
+};
+
+struct DecodeArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  const int* cache_len;
+  const int* q_pos;
+  float* part_o;     // [B][Hq][S][d_h]
+  float* part_ml;    // [B][Hq][S][2]
+  unsigned long long* counters;
+  int64_t qs_b, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_h;
+  int B, Lmax, Hq, Hkv;
+  int r;          // Hq / Hkv (<= 16)
+  int S;          // splits
+  int split_len;  // keys per split, multiple of kDecodeBN
+  float scale_log2;
+  int cut[kMaxGroups];
+};
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s);
+
+}  // namespace wp

@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI: the library loads and exports every function the
+header declares; host-only calls (cutoff table, tiling, host tile classifier)
+agree bit-exactly with the oracle; invalid arguments are rejected before any
+HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import rope_positional_encoding_amd as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "waveprune.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 13
+    L = ctypes.CDLL(W.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(W._SIGNATURES), "binding signatures out of sync with the header"
+
+
+@pytest.mark.parametrize("theta", [10.0, 100.0, 500.0, 1e4, 5e5, 1e6, 1e7])
+@pytest.mark.parametrize("d_h", [8, 16, 64, 128])
+@pytest.mark.parametrize("s", [1.0, 2.0, 4.0, 8.0])
+def test_group_cutoffs_match_oracle(theta, d_h, s):
+    for G in (2, 4, 8, 16, 32):
+        if d_h % G:
+            continue
+        got = W.group_cutoffs(theta, d_h, G, s)
+        ref = O.group_cutoffs(theta, d_h, G, s)
+        assert got == [int(v) for v in ref]
+
+
+def test_group_cutoffs_clamp_never_prune():
+    # d_h = 128, theta = 1e12, scale 1e6: low channels exceed 2^31 - 1
+    got = W.group_cutoffs(1e12, 128, 16, 1e6)
+    assert got[-1] == W.NEVER_PRUNE
+    assert got == [int(v) for v in O.group_cutoffs(1e12, 128, 16, 1e6)]
+
+
+def test_tiling_queries():
+    assert W.prefill_tiling(128, 16) == (32, 32)
+    assert W.prefill_tiling(64, 32) == (32, 32)
+    assert W.decode_tiling(128, 16) == 32
+    with pytest.raises(W.WPError) as e:
+        W.prefill_tiling(96, 16)
+    assert e.value.status == -3
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 256, 1000, 4096])
+@pytest.mark.parametrize("cfg", [(64, 16, 1e4, 1.0), (128, 16, 1e6, 1.0), (128, 32, 1e6, 1.0),
+                                 (128, 16, 1e6, 4.0), (64, 32, 100.0, 1.0), (128, 16, 30.0, 1.0)])
+def test_host_prefill_classifier_matches_oracle(n, cfg):
+    d_h, G, theta, s = cfg
+    cut = [int(v) for v in O.group_cutoffs(theta, d_h, G, s)]
+    BM, BN = W.prefill_tiling(d_h, G)
+    got = W.prefill_tile_counts(n, d_h, G, cut)
+    c, v = O.prefill_tile_counts(n, BM, BN, np.array(cut))
+    assert got == list(c.ravel()) + [v]
+
+
+def test_host_prefill_classifier_32k_and_128k():
+    for n, s in ((32768, 1.0), (131072, 4.0)):
+        cut = [int(v) for v in O.group_cutoffs(1e6, 128, 16, s)]
+        got = W.prefill_tile_counts(n, 128, 16, cut)
+        c, v = O.prefill_tile_counts(n, 32, 32, np.array(cut))
+        assert got == list(c.ravel()) + [v]
+
+
+@pytest.mark.parametrize("q_pos,L", [(32768, 32768), (32767, 32768), (5000, 33), (40, 1), (0, 1)])
+def test_host_decode_classifier_matches_oracle(q_pos, L):
+    for d_h, G, theta in ((128, 16, 1e6), (128, 32, 1e6), (64, 16, 1e3)):
+        cut = [int(v) for v in O.group_cutoffs(theta, d_h, G)]
+        got = W.decode_tile_counts(q_pos, L, d_h, G, cut)
+        c, v = O.decode_tile_counts(q_pos, L, W.decode_tiling(d_h, G), np.array(cut))
+        assert got == list(c.ravel()) + [v]
+
+
+def test_classifier_rejects_bad_tables():
+    with pytest.raises(W.WPError) as e:
+        W.prefill_tile_counts(100, 128, 16, [5, 4, 6, 7, 8, 9, 10, 11])
+    assert e.value.status == -6
+    with pytest.raises(W.WPError) as e:
+        W.prefill_tile_counts(100, 128, 16, [-1, 4, 6, 7, 8, 9, 10, 11])
+    assert e.value.status == -6
+
+
+# ---- validation happens before any HIP call: fake aligned device pointers ----
+FAKE = ctypes.c_void_p(0x7F0000000000)   # never dereferenced: every call below fails validation
+
+
+def _strides(n):
+    return (ctypes.c_int64 * n)(*([8] * n))
+
+
+def _prefill(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, n=64, Hq=4, Hkv=2, d_h=128,
+                strides=_strides(12), cut=(ctypes.c_int32 * 8)(*range(8)), G=16, flags=0,
+                counters=None, stream=None)
+    args.update(kw)
+    return W.lib().wp_prefill(*args.values())
+
+
+def test_prefill_validation_codes():
+    assert _prefill(q=None) == -1
+    assert _prefill(d_h=96) == -3
+    assert _prefill(G=8) == -3
+    assert _prefill(Hq=3) == -2
+    assert _prefill(n=0) == -2
+    assert _prefill(q=ctypes.c_void_p(0x7F0000000008)) == -4
+    st = _strides(12)
+    st[4] = 12
+    assert _prefill(strides=st) == -4
+    assert _prefill(cut=(ctypes.c_int32 * 8)(9, 8, 7, 6, 5, 4, 3, 2)) == -6
+    assert "non-decreasing" in W.lib().wp_last_error().decode()
+    assert _prefill(cut=None) == -1
+    assert _prefill(flags=2) == -1                       # COUNT without counters
+    assert _prefill(flags=8) == -6                       # unknown flag
+
+
+def _decode(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, cl=FAKE, qp=FAKE, B=2, Lmax=100, Hq=4, Hkv=2,
+                d_h=128, strides=_strides(10), cut=(ctypes.c_int32 * 8)(*range(8)), G=16,
+                splits=0, ws=FAKE, ws_bytes=1 << 30, flags=0, counters=None, stream=None)
+    args.update(kw)
+    return W.lib().wp_decode(*args.values())
+
+
+def test_decode_validation_codes():
+    assert _decode(ws=None) == -1
+    assert _decode(d_h=80) == -3
+    assert _decode(Hq=64, Hkv=2) == -3                   # more than 16 heads per kv head
+    assert _decode(ws_bytes=16) == -5
+    assert _decode(ws=ctypes.c_void_p(0x7F0000000010)) == -4
+    assert _decode(splits=-1) == -6
+    assert _decode(Lmax=0) == -2
+
+
+def test_rope_validation_codes():
+    L = W.lib()
+    s3 = _strides(3)
+    assert L.wp_rope_apply(FAKE, 2, FAKE, 1, 8, 2, 128, s3, s3, None, 1e4, 1.0, None) == -6
+    assert L.wp_rope_apply(FAKE, 0, FAKE, 1, 8, 2, 128, s3, s3, None, -1.0, 1.0, None) == -6
+    assert L.wp_rope_apply(FAKE, 0, FAKE, 1, 8, 2, 128, s3, s3, None, 1e4, 0.0, None) == -6
+    assert L.wp_rope_apply(FAKE, 0, FAKE, 1, 8, 2, 96, s3, s3, None, 1e4, 1.0, None) == -3
+    assert L.wp_rope_apply(FAKE, 1, FAKE, 1, 8, 2, 128, s3, s3, None, 1e4, 1.0, None) == -6  # f32 in place
+    assert L.wp_rope_apply(None, 0, FAKE, 1, 8, 2, 128, s3, s3, None, 1e4, 1.0, None) == -1
+
+
+def test_status_strings():
+    L = W.lib()
+    for s in range(0, -8, -1):
+        assert L.wp_status_string(s)
+    assert L.wp_version().decode().count(".") == 2

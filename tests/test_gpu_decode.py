@@ -1,0 +1,121 @@
+"""GPU parity of wp_decode against the oracle (split-KV, suffix-K loads)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rope_positional_encoding_amd as W
+from rope_positional_encoding_amd import synth
+from gpu_util import Timer, bf16_to_np, bits_to_dev, compare, dev, say, separation, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected(q_pos, cache_len, d_h, G, cut, Hkv):
+    BN = W.decode_tiling(d_h, G)
+    tot = np.zeros(3 * (d_h // G) + 1, dtype=np.int64)
+    for qp, L in zip(q_pos, cache_len):
+        c, v = O.decode_tile_counts(int(qp), int(L), BN, np.asarray(cut))
+        tot += np.concatenate([c.ravel(), [v]]) * Hkv
+    return tot
+
+
+# B, Lmax, Hq, Hkv, d, G, theta, cache_len per batch, q_pos offset vs cache_len, splits
+SMALL = [
+    (1, 1, 1, 1, 64, 16, 1e4, [1], 0, 0),
+    (3, 300, 4, 1, 64, 32, 100.0, [300, 31, 1], 0, 0),
+    (2, 1000, 16, 2, 128, 16, 1e3, [1000, 333], 1, 3),
+    (4, 5000, 32, 8, 128, 16, 1e4, [5000, 4097, 33, 2049], -1, 0),
+    (2, 2000, 16, 1, 128, 32, 300.0, [1999, 64], 1, 1),
+    (2, 700, 8, 4, 128, 16, 30.0, [700, 650], 0, 5),
+]
+
+
+@pytest.mark.parametrize("B,Lmax,Hq,Hkv,d,G,theta,lens,qoff,splits", SMALL)
+@pytest.mark.parametrize("dense", [False, True])
+def test_decode_small(B, Lmax, Hq, Hkv, d, G, theta, lens, qoff, splits, dense):
+    say("decode B=%d Lmax=%d Hq=%d Hkv=%d d=%d G=%d theta=%g lens=%s qoff=%d splits=%d dense=%s"
+        % (B, Lmax, Hq, Hkv, d, G, theta, lens, qoff, splits, dense))
+    seed = 2000 + Lmax + Hq
+    q = synth.normal_bits(seed, 0, B, (Hq, d))
+    kc = synth.normal_bits(seed, 1, B * Lmax, (Hkv, d))
+    vc = synth.normal_bits(seed, 2, B * Lmax, (Hkv, d))
+    # q_pos = cache_len + qoff (qoff = -1: the query's own key is the last cached one)
+    q_pos = [L + qoff if L + qoff >= L - 1 else L - 1 for L in lens]
+    cut = [int(c) for c in O.group_cutoffs(theta, d, G)]
+    qt = bits_to_dev(q, (B, Hq, d))
+    kt = bits_to_dev(kc, (B, Lmax, Hkv, d))
+    vt = bits_to_dev(vc, (B, Lmax, Hkv, d))
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    qp = torch.tensor(q_pos, dtype=torch.int32, device=dev())
+    cnt = torch.zeros(3 * (d // G) + 1, dtype=torch.int64, device=dev())
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=dev())
+    W.decode(qt, kt, vt, cl, qp, None if dense else cut, G, dense=dense, num_splits=splits,
+             counters=cnt, out=o)
+    torch.cuda.synchronize()
+    got = bf16_to_np(o)
+    dim_cut = O.dim_cutoffs_dense(d) if dense else O.dim_cutoffs_grouped(np.array(cut), G)
+    for b in range(B):
+        sl = slice(b * Lmax, (b + 1) * Lmax)
+        ref = O.decode(to_f64(q[b]), to_f64(kc[sl]), to_f64(vc[sl]), q_pos[b], lens[b], dim_cut)
+        compare(got[b], ref, "decode b=%d L=%d" % (b, lens[b]))
+    exp = _expected(q_pos, lens, d, G, [O.NEVER] * (d // G) if dense else cut, Hkv)
+    assert np.array_equal(cnt.cpu().numpy(), exp), (cnt.cpu().numpy(), exp)
+
+
+def test_decode_split_count_invariance():
+    B, Lmax, Hq, Hkv, d, G = 2, 3000, 8, 2, 128, 16
+    q = bits_to_dev(synth.normal_bits(9, 0, B, (Hq, d)), (B, Hq, d))
+    k = bits_to_dev(synth.normal_bits(9, 1, B * Lmax, (Hkv, d)), (B, Lmax, Hkv, d))
+    v = bits_to_dev(synth.normal_bits(9, 2, B * Lmax, (Hkv, d)), (B, Lmax, Hkv, d))
+    cl = torch.tensor([3000, 2500], dtype=torch.int32, device=dev())
+    qp = torch.tensor([3000, 2500], dtype=torch.int32, device=dev())
+    cut = W.group_cutoffs(1e4, d, G)
+    outs = [W.decode(q, k, v, cl, qp, cut, G, num_splits=s) for s in (1, 2, 7, 0)]
+    again = W.decode(q, k, v, cl, qp, cut, G, num_splits=7)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[2], again)                  # deterministic
+    base = outs[0].float()
+    for o in outs[1:]:
+        assert (o.float() - base).abs().max().item() < 2e-2
+
+
+def test_workload_decode32k():
+    w = synth.WORKLOADS["decode32k"]
+    B, L, Hq, Hkv, d = w.B, w.n, w.Hq, w.Hkv, w.d_h
+    say("workload decode32k: B=%d L=%d Hq=%d Hkv=%d d=%d G=%d q_pos=%d" % (B, L, Hq, Hkv, d, w.G, w.q_pos))
+    with Timer("inputs"):
+        q_raw = synth.normal_bits(w.seed, synth.TID_Q, B, (Hq, d))
+        k_raw = synth.normal_bits(w.seed, synth.TID_K, B * L, (Hkv, d))
+        v_bits = synth.normal_bits(w.seed, synth.TID_V, B * L, (Hkv, d))
+    cut = W.group_cutoffs(w.theta, d, w.G)
+    with Timer("gpu rope+decode"):
+        qd = bits_to_dev(q_raw, (B, 1, Hq, d))
+        kd = bits_to_dev(k_raw, (B, L, Hkv, d))
+        vd = bits_to_dev(v_bits, (B, L, Hkv, d))
+        qpos_t = torch.full((B,), w.q_pos, dtype=torch.int64, device=dev())
+        qr = W.rope_apply(qd, w.theta, w.pos_scale, pos_start=qpos_t)[:, 0]
+        kr = W.rope_apply(kd, w.theta, w.pos_scale)
+        del kd
+        cl = torch.full((B,), L, dtype=torch.int32, device=dev())
+        qp = torch.full((B,), w.q_pos, dtype=torch.int32, device=dev())
+        cnt = torch.zeros(3 * (d // w.G) + 1, dtype=torch.int64, device=dev())
+        o = W.decode(qr, kr, vd, cl, qp, cut, w.G, counters=cnt)
+        torch.cuda.synchronize()
+    got = bf16_to_np(o)
+    exp = _expected([w.q_pos] * B, [L] * B, d, w.G, cut, Hkv)
+    say("  counters", cnt.cpu().numpy().tolist())
+    assert np.array_equal(cnt.cpu().numpy(), exp)
+    dim_cut = O.dim_cutoffs_grouped(np.array(cut), w.G)
+    refs, dens = [], []
+    with Timer("oracle"):
+        for b in range(B):
+            kb = O.rope(to_f64(k_raw[b * L:(b + 1) * L]), np.arange(L), w.theta)
+            qb = O.rope(to_f64(q_raw[b:b + 1]), np.array([w.q_pos]), w.theta)[0]
+            vb = to_f64(v_bits[b * L:(b + 1) * L])
+            refs.append(O.decode(qb, kb, vb, w.q_pos, L, dim_cut))
+            if b < 2:
+                dens.append(O.decode(qb, kb, vb, w.q_pos, L, O.dim_cutoffs_dense(d)))
+    ref = np.stack(refs)
+    compare(got, ref, "decode32k O")
+    separation(ref[:2], np.stack(dens), "grouped vs dense (2 seqs)")
