@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (3 launches): a kernel of known "
+                         "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -154,6 +157,13 @@ def main():
     def randn(*shape):
         return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("bench: allocating inputs")
     q_raw = randn(1, n, Hq, d)
     k_raw = randn(1, n, Hkv, d)

@@ -17,10 +17,13 @@ LIB = os.path.join(PKG, "libwaveprune.so")
 SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed FP32 VALU forms are switched off for all device code.
+# Packed FP32 VALU forms are switched off for all device code.  IEEE mode is
+# off (no signaling-NaN quieting before min/max, so row maxima become
+# v_max3 chains); the kernels never produce or consume NaNs.
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

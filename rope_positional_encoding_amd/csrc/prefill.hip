@@ -4,7 +4,7 @@
 // within its cutoff; pruned terms are 0 and the key stays in the softmax
 // (WavePrune reading notes on cc.laoqi.cc, section 2.1, Eq. (6)).  Head dims
 // are grouped (G = 16 or 32) and a group uses the largest cutoff inside it
-// (section 2.3, Eq. (8)).  Each (32-query x 32-key) tile is classified per
+// (section 2.3, Eq. (8)).  Each (32-query x 64-key) tile is classified per
 // group from its distance range [l_D, r_D]: skip, partial or full
 // (section 2.3 table).  Because the cutoffs are non-decreasing two split
 // points describe a tile: groups [0, splitL) skip, [splitL, splitR) partial,
@@ -13,22 +13,28 @@
 // gfx950 design (not the pages' A100 design):
 //  * The logits are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: one MFMA contracts exactly 16 head dims, so a
-//    G = 16 group is one MFMA per 32x32 tile and G = 32 is two.  In S^T the
+//    G = 16 group is one MFMA per 32x32 block and G = 32 is two.  In S^T the
 //    lane owns one query column, so row max / row sum need one cross-half
 //    exchange only, and the probabilities are already laid out as the B
 //    operand of O^T = V^T P^T.
-//  * Skipped groups issue no MFMA; full groups chain into one accumulator
-//    (the "suffix" GEMM); a partial group gets its own accumulator, is masked
-//    with dist <= cutoff, then added.  The branches are wave-uniform scalar
-//    branches, so no per-(splitL, splitR) code specialization is needed.
+//  * Skipped groups issue no MFMA; the full groups run as one MFMA chain
+//    from the highest group down, leaving the chain with one wave-uniform
+//    scalar branch at splitR (the "suffix" GEMM); a partial group gets its
+//    own accumulator, is masked with dist <= cutoff, then added, on a
+//    separate path that only boundary tiles take.  No per-(splitL, splitR)
+//    code specialization is needed.
 //  * A workgroup is 4 waves that share one kv head and one key range: with
 //    GQA ratio >= 4 the waves are 4 query heads over the same 32 queries
 //    (identical tile classes, K/V staged once in LDS for all four).
 //  * K is staged row-major in LDS (row pad 16 B: conflict-free 16-byte MFMA
 //    operand reads); V is written transposed (V^T) with a key permutation
 //    that matches the S^T register layout, so both MFMA operands of P.V are
-//    single 16-byte LDS reads.  The next K/V tile is prefetched into
-//    registers while the current one is consumed.
+//    single 16-byte LDS reads.  LDS holds two stages: while tile t is
+//    consumed, tile t+1 is written into the other stage and tile t+2 is in
+//    flight from HBM into registers; one barrier per tile.
+//  * The running max is refreshed (and O rescaled) only when it grows by more
+//    than 8 in log2 units, so every probability stays below 2^8; the final
+//    O / l and the LSE are unaffected.
 //  * Workgroups run heaviest (last query blocks) first; kv head is the
 //    fastest-varying block index so that on 8 kv heads each XCD (blocks are
 //    dealt round-robin to the 8 XCDs) keeps one kv head's K/V in its L2.
@@ -39,18 +45,45 @@ namespace wp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileKeys = 64;     // keys per LDS tile (two 32-key MFMA blocks)
+// dword 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kTileKeys = 64;     // keys per tile: two 32-key MFMA blocks, one class per group
 
 __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (nearest even), one v_cvt_pk_bf16_f32
 __device__ inline unsigned int pack_bf16x2(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// A raw buffer resource for [p, p + bytes) held in scalar registers: the
+// base and size are wave-uniform by construction, readfirstlane makes that
+// explicit so loads through it need no per-lane waterfall loop.
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
+// Combine x of lanes l and l ^ 32 (the two halves that hold one query
+// column) with v_permlane32_swap, no LDS round trip.  Swapping rows 2-3 of
+// (x) with rows 0-1 of (x) leaves every lane with x_lo in one result and
+// x_hi in the other, so max / sum of the pair is the same in both halves.
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Row (key) of register r of a 32x32 MFMA output block for lane half hh.
@@ -80,8 +113,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int VITEMS = 16 * CPR;                     // (key quad, chunk) items
   static_assert(KITEMS >= 1 && VITEMS <= kThreads, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[kTileKeys * KS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[D * VS];
+  // two LDS stages: tile t is consumed from stage t&1 while tile t+1 is
+  // written into the other one
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][kTileKeys * KS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][D * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,11 +135,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int n = a.n;
   const int h = kvh * a.r + hg * a.HPW + (wave % a.HPW);
   const int i0_wg = qblk * a.QB;
-  const int i0w = i0_wg + (wave / a.HPW) * 32;
+  // wave-uniform control values, pinned to scalar registers
+  const int i0w = __builtin_amdgcn_readfirstlane(i0_wg + (wave / a.HPW) * 32);
   const bool wave_valid = i0w < n;
-  const int i1w = min(n, i0w + 32) - 1;
+  const int i1w = __builtin_amdgcn_readfirstlane(min(n, i0w + 32) - 1);
   const int kend = min(n, i0_wg + a.QB);
-  const int nk = (kend + kTileKeys - 1) / kTileKeys;
+  const int nk = __builtin_amdgcn_readfirstlane((kend + kTileKeys - 1) / kTileKeys);
 
   const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
   const bf16* vbase = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
@@ -121,41 +157,50 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       qr[c] = (i < n) ? *reinterpret_cast<const u32x4*>(qp + c * 16) : zero;
   }
 
-  // register staging of the next K/V tile
+  // register staging of the next K/V tile.  Tile rows are fetched with raw
+  // buffer loads whose resource starts at the tile's first row and ends
+  // after row n-1: rows past the end of the sequence read as zero, and the
+  // per-thread byte offsets are loop invariant.
   u32x4 kreg[KITEMS];
   u32x4 vreg[4];
   const int v_kq = tid & 15;
   const int v_dc = tid >> 4;
   const bool v_active = tid < VITEMS;
+  const int krow_b = (int)(a.ks_t * 2);     // bytes between consecutive keys
+  const int vrow_b = (int)(a.vs_t * 2);
+  int koff[KITEMS];
+#pragma unroll
+  for (int it = 0; it < KITEMS; ++it) {
+    const int idx = tid + it * kThreads;
+    koff[it] = (idx / CPR) * krow_b + (idx % CPR) * 16;
+  }
+  const int voff = 4 * v_kq * vrow_b + v_dc * 16;
 
   auto load_tile = [&](int j0) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int rows = n - j0;                                  // >= 1
+    const __amdgpu_buffer_rsrc_t kr =
+        uniform_rsrc(kbase + (int64_t)j0 * a.ks_t, (rows - 1) * krow_b + 2 * D);
+    const __amdgpu_buffer_rsrc_t vr =
+        uniform_rsrc(vbase + (int64_t)j0 * a.vs_t, (rows - 1) * vrow_b + 2 * D);
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int idx = tid + it * kThreads;
-      const int key = idx / CPR;
-      const int dc = idx % CPR;
-      const int j = j0 + key;
-      kreg[it] = (j < n) ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * a.ks_t + dc * 8)
-                         : zero;
-    }
+    for (int it = 0; it < KITEMS; ++it)
+      kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[it], 0, 0);
     if (v_active) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = j0 + 4 * v_kq + q4;
-        vreg[q4] = (j < n) ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * a.vs_t + v_dc * 8)
-                           : zero;
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        vreg[q4] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + q4 * vrow_b, 0, 0);
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    bf16* k_s = sK[stage];
+    bf16* v_s = sV[stage];
 #pragma unroll
     for (int it = 0; it < KITEMS; ++it) {
       const int idx = tid + it * kThreads;
       const int key = idx / CPR;
       const int dc = idx % CPR;
-      *reinterpret_cast<u32x4*>(&sK[key * KS + dc * 8]) = kreg[it];
+      *reinterpret_cast<u32x4*>(&k_s[key * KS + dc * 8]) = kreg[it];
     }
     if (v_active) {
       // vreg[q] holds dims [8dc, 8dc+8) of key 4kq+q as 4 dwords of 2 dims;
@@ -165,18 +210,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) {
         const unsigned int w0 = vreg[0][e], w1 = vreg[1][e], w2 = vreg[2][e], w3 = vreg[3][e];
         u32x2 even, odd;
-        even[0] = (w0 & 0xffffu) | (w1 << 16);
-        even[1] = (w2 & 0xffffu) | (w3 << 16);
-        odd[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        odd[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+        even[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // (w0.lo, w1.lo)
+        even[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+        odd[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);    // (w0.hi, w1.hi)
+        odd[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
         const int d = v_dc * 8 + 2 * e;
-        *reinterpret_cast<u32x2*>(&sV[d * VS + pos]) = even;
-        *reinterpret_cast<u32x2*>(&sV[(d + 1) * VS + pos]) = odd;
+        *reinterpret_cast<u32x2*>(&v_s[d * VS + pos]) = even;
+        *reinterpret_cast<u32x2*>(&v_s[(d + 1) * VS + pos]) = odd;
       }
     }
   };
 
-  float m_i = -INFINITY;   // running max, log2 domain
+  float m_i = -INFINITY;   // running max (log2 domain), possibly stale by < 8
   float l_i = 0.f;         // running sum (this lane's half of the keys)
   f32x16 o[ND];
 #pragma unroll
@@ -192,34 +237,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 
   const float sl2 = a.scale_log2;
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
   load_tile(0);
+  store_tile(0);
+  if (nk > 1) load_tile(kTileKeys);
+  __syncthreads();
 
   for (int it = 0; it < nk; ++it) {
     const int j0 = it * kTileKeys;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < nk) load_tile(j0 + kTileKeys);
-    if (!wave_valid || j0 > i1w) continue;
-
-    f32x16 s[2];
-    bool vis[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int jb0 = j0 + 32 * kb;
-      vis[kb] = jb0 <= i1w;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      if (!vis[kb]) continue;
-      const int jb1 = min(n - 1, jb0 + 31);
-      const int lD = max(0, i0w - jb1);
-      const int rD = i1w - jb0;
+    const int stage = it & 1;
+    if (wave_valid && j0 <= i1w) {
+      // ---- classify the (32 queries x 64 keys) tile ----
+      const int j1 = min(n - 1, j0 + kTileKeys - 1);
+      const int lD = max(0, i0w - j1);
+      const int rD = i1w - j0;
+      // cutoffs are non-decreasing: splitL / splitR = 1 + last group below
       int sL = 0, sR = 0;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        sL += a.cut[g] < lD;
-        sR += a.cut[g] < rD;
+        sL = (a.cut[g] < lD) ? g + 1 : sL;
+        sR = (a.cut[g] < rD) ? g + 1 : sR;
       }
+      sL = __builtin_amdgcn_readfirstlane(sL);
+      sR = __builtin_amdgcn_readfirstlane(sR);
       if (COUNT) {
         ++cnt_vis;
 #pragma unroll
@@ -229,91 +270,125 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
           cnt[g][2] += (g >= sR);
         }
       }
-      const bf16* krow = &sK[(32 * kb + l32) * KS + hh * 8];
+
+      // ---- S^T = K Q^T: full groups [sR, NG) as one chain, highest first ----
+      const bf16* k0 = &sK[stage][l32 * KS + hh * 8];
+      const bf16* k1 = k0 + 32 * KS;
+      f32x16 s0, s1;
+      if (sR < NG) {
+        {
+          constexpr int c0 = (NG - 1) * GC;
+          s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + c0 * 16), qr[c0], zero16);
+          s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + c0 * 16), qr[c0], zero16);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (g < sL) continue;                       // skip: no MFMA
-        if (g >= sR) {                              // full: chain into S
+          for (int c = 1; c < GC; ++c) {
+            s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + (c0 + c) * 16), qr[c0 + c], s0);
+            s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + (c0 + c) * 16), qr[c0 + c], s1);
+          }
+        }
+#pragma unroll
+        for (int g = NG - 2; g >= 0; --g) {
+          if (g < sR) break;
 #pragma unroll
           for (int c = 0; c < GC; ++c) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (g * GC + c) * 16);
-            s[kb] = mfma32(ka, qr[g * GC + c], s[kb]);
+            const int cc = g * GC + c;
+            s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + cc * 16), qr[cc], s0);
+            s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + cc * 16), qr[cc], s1);
           }
-        } else {                                    // partial: compute, mask, add
-          f32x16 t;
+        }
+      } else {
+        s0 = zero16;
+        s1 = zero16;
+      }
+
+      // ---- partial groups [sL, sR): compute, mask dist <= cutoff, add ----
+      if (sL < sR) {
+        const int base = (i0w + l32) - j0;     // dist = base - (32kb + out_row(r))
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = 0.f;
-#pragma unroll
-          for (int c = 0; c < GC; ++c) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(krow + (g * GC + c) * 16);
-            t = mfma32(ka, qr[g * GC + c], t);
-          }
-          const int base = (i0w + l32) - jb0;       // dist = base - out_row(r)
+        for (int g = NG - 1; g >= 0; --g) {
+          if (g >= sR || g < sL) continue;
           const int cg = a.cut[g];
+          f32x16 t = zero16;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[kb][r] += (base - out_row(r, hh) <= cg) ? t[r] : 0.f;
+          for (int c = 0; c < GC; ++c) {
+            const int cc = g * GC + c;
+            t = mfma32(*reinterpret_cast<const u32x4*>(k0 + cc * 16), qr[cc], t);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s0[r] += (base - out_row(r, hh) <= cg) ? t[r] : 0.f;
+          t = zero16;
+#pragma unroll
+          for (int c = 0; c < GC; ++c) {
+            const int cc = g * GC + c;
+            t = mfma32(*reinterpret_cast<const u32x4*>(k1 + cc * 16), qr[cc], t);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s1[r] += (base - 32 - out_row(r, hh) <= cg) ? t[r] : 0.f;
         }
       }
-      if (jb0 + 31 > i0w) {                         // crosses the diagonal
-        const int base = (i0w + l32) - jb0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (out_row(r, hh) > base) s[kb][r] = -INFINITY;
-      }
-    }
 
-    // online softmax (log2 domain, scale folded into the exponent)
-    float mx = -INFINITY;
+      // ---- causal mask on tiles that reach past the wave's first query ----
+      if (j0 + kTileKeys - 1 > i0w) {
+        const int base = (i0w + l32) - j0;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (vis[kb]) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 0; r < 16; ++r) {
+          if (out_row(r, hh) > base) s0[r] = -INFINITY;
+          if (32 + out_row(r, hh) > base) s1[r] = -INFINITY;
+        }
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
-    l_i *= alpha;
-    u32x4 p[4];
+
+      // ---- online softmax, log2 domain; rescale O only when the running
+      //      max grows by more than 8 (so every p stays <= 2^8) ----
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!vis[kb]) continue;
-      float e[16];
+      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);   // v_max3 chain
+      mx = halves_max(mx);
+      const float m_cand = mx * sl2;
+      if (__any(m_cand > m_i + 8.f)) {
+        const float m_new = fmaxf(m_i, m_cand);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+        l_i *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], sl2, -m_use));
-        l_i += e[r];
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_i = m_use;
       }
+      u32x4 p[4];
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          p[2 * kb + c][w] = pack_bf16x2(e[8 * c + 2 * w], e[8 * c + 2 * w + 1]);
-    }
-    if (__any(m_new > m_i)) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    m_i = m_new;
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * c + 2 * w;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -m_i));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], sl2, -m_i));
+          const float f0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -m_i));
+          const float f1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], sl2, -m_i));
+          l_i += (e0 + e1) + (f0 + f1);
+          p[c][w] = pack_bf16x2(e0, e1);
+          p[2 + c][w] = pack_bf16x2(f0, f1);
+        }
 
-    // O^T += V^T P^T
+      // ---- O^T += V^T P^T ----
+      const bf16* vs = &sV[stage][l32 * VS + hh * 8];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      if (!vis[kc >> 1]) continue;
+      for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(&sV[(db * 32 + l32) * VS + kc * 16 + hh * 8]);
-        o[db] = mfma32(va, p[kc], o[db]);
-      }
+        for (int db = 0; db < ND; ++db) {
+          const u32x4 va = *reinterpret_cast<const u32x4*>(vs + db * 32 * VS + kc * 16);
+          o[db] = mfma32(va, p[kc], o[db]);
+        }
     }
+
+    // ---- stage the next tile; prefetch the one after ----
+    if (it + 1 < nk) store_tile(stage ^ 1);
+    if (it + 2 < nk) load_tile((it + 2) * kTileKeys);
+    __syncthreads();
   }
 
   if (wave_valid) {
-    const float l_tot = l_i + __shfl_xor(l_i, 32);
+    const float l_tot = halves_sum(l_i);
     const int i = i0w + l32;
     if (i < n) {
       const float inv = 1.f / l_tot;

@@ -18,10 +18,11 @@ constexpr int kMaxGroups = 8;       // d_h / G for d_h <= 128, G >= 16
 constexpr int kMaxChannels = 64;    // d_h / 2 for d_h <= 128
 
 // Tile geometry shared by the kernels, the host classifier and the tiling
-// queries.  Prefill: a tile is 32 queries of one head x 32 keys (one
-// 32x32 MFMA output block); decode: a key block of 32 keys.
+// queries.  Prefill: a tile is 32 queries of one head x 64 keys (two 32x32
+// MFMA output blocks that share one class per group); decode: a key block of
+// 32 keys.
 constexpr int kPrefillBM = 32;
-constexpr int kPrefillBN = 32;
+constexpr int kPrefillBN = 64;
 constexpr int kDecodeBN = 32;
 
 struct RopeArgs {

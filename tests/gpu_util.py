@@ -42,7 +42,10 @@ def compare(got: np.ndarray, ref: np.ndarray, label: str, max_abs=MAX_ABS, mean_
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), "%s: non-finite outputs" % label
     mx, mn = float(err.max()), float(err.mean())
-    say("%-40s max_abs=%.3e mean_abs=%.3e (n=%d)" % (label, mx, mn, err.size))
+    # the part of the error that is only the bf16 rounding of the output
+    floor = float(np.abs(synth.bf16_round(ref.astype(np.float32)).astype(np.float64) - ref).max())
+    say("%-40s max_abs=%.3e mean_abs=%.3e (n=%d; bf16 output rounding alone: max %.3e)"
+        % (label, mx, mn, err.size, floor))
     assert mx <= max_abs and mn <= mean_abs, "%s: max %.3e mean %.3e" % (label, mx, mn)
     return mx, mn
 
@@ -87,11 +90,19 @@ def to_f64(x: np.ndarray) -> np.ndarray:
     return x.astype(np.float64)
 
 
-def oracle_prefill_rows(w, q_raw_rows, k_raw, v_bits, rows, dim_cut, b=0):
+def round_bf16_f64(x: np.ndarray) -> np.ndarray:
+    return synth.bf16_round(x.astype(np.float32)).astype(np.float64)
+
+
+def oracle_prefill_rows(w, q_raw_rows, k_raw, v_bits, rows, dim_cut, b=0, bf16_in=False):
     """Oracle output rows [len(rows), Hq, d] of batch b: RoPE in float64 of the
-    raw inputs at positions 0..n-1, then the rule given by dim_cut."""
+    raw inputs at positions 0..n-1, then the rule given by dim_cut.  With
+    bf16_in, the rotated q and k are rounded to bf16 (nearest even) first:
+    the precision the attention kernel takes its inputs in."""
     n = w.n
     kr = O.rope(to_f64(k_raw[b * n:(b + 1) * n]), np.arange(n), w.theta, w.pos_scale)
     qr = O.rope(to_f64(q_raw_rows), np.asarray(rows), w.theta, w.pos_scale)
+    if bf16_in:
+        kr, qr = round_bf16_f64(kr), round_bf16_f64(qr)
     v = to_f64(v_bits[b * n:(b + 1) * n])
     return O.prefill(qr, kr, v, dim_cut, rows=rows, q_is_rows=True)

@@ -51,8 +51,8 @@ def test_group_cutoffs_clamp_never_prune():
 
 
 def test_tiling_queries():
-    assert W.prefill_tiling(128, 16) == (32, 32)
-    assert W.prefill_tiling(64, 32) == (32, 32)
+    assert W.prefill_tiling(128, 16) == (32, 64)
+    assert W.prefill_tiling(64, 32) == (32, 64)
     assert W.decode_tiling(128, 16) == 32
     with pytest.raises(W.WPError) as e:
         W.prefill_tiling(96, 16)
@@ -75,7 +75,8 @@ def test_host_prefill_classifier_32k_and_128k():
     for n, s in ((32768, 1.0), (131072, 4.0)):
         cut = [int(v) for v in O.group_cutoffs(1e6, 128, 16, s)]
         got = W.prefill_tile_counts(n, 128, 16, cut)
-        c, v = O.prefill_tile_counts(n, 32, 32, np.array(cut))
+        BM, BN = W.prefill_tiling(128, 16)
+        c, v = O.prefill_tile_counts(n, BM, BN, np.array(cut))
         assert got == list(c.ravel()) + [v]
 
 

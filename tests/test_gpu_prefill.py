@@ -129,10 +129,19 @@ def _run_workload(name, nrows_override=None, sep_rows=0):
     got = bf16_to_np(o[0, torch.from_numpy(rows).to(dev())]).reshape(len(rows), w.Hq, w.d_h)
     del o, qr, kr, vd
     q_rows = q_raw[rows]
-    with Timer("oracle %d rows" % len(rows)):
-        ref = oracle_prefill_rows(w, q_rows, k_raw, v_bits, rows,
-                                  O.dim_cutoffs_grouped(np.array(cut), w.G))
-    compare(got, ref, "%s O (%d rows)" % (name, len(rows)))
+    dim_cut = O.dim_cutoffs_grouped(np.array(cut), w.G)
+    with Timer("oracle %d rows (x2)" % len(rows)):
+        # bf16-in reference: the oracle's rotated q, k rounded to bf16, the
+        # precision the attention kernel consumes
+        ref_b = oracle_prefill_rows(w, q_rows, k_raw, v_bits, rows, dim_cut, bf16_in=True)
+        ref = oracle_prefill_rows(w, q_rows, k_raw, v_bits, rows, dim_cut)
+    compare(got, ref_b, "%s O vs bf16-in oracle (%d rows)" % (name, len(rows)))
+    # end to end against float64 RoPE: the gate plus the shift that rounding
+    # the rotated inputs to bf16 alone causes in the oracle
+    shift = np.abs(ref_b - ref)
+    say("  oracle shift from bf16 rotated inputs: max %.3e mean %.3e" % (shift.max(), shift.mean()))
+    compare(got, ref, "%s O vs fp64-RoPE oracle" % name,
+            max_abs=2e-2 + float(shift.max()), mean_abs=2e-3 + float(shift.mean()))
     if sep_rows:
         sub = rows[np.linspace(0, len(rows) - 1, sep_rows).astype(int)]
         pick = np.searchsorted(rows, sub)
