@@ -36,11 +36,25 @@ __device__ inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (nearest even), one v_cvt_pk_bf16_f32
 __device__ inline unsigned int pack_bf16x2(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return (unsigned int)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned int)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// dword 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts
+constexpr int kBufferFlags = 0x00020000;
+
+// A raw buffer resource for [p, p + bytes) in scalar registers (base and size
+// are wave-uniform; readfirstlane makes that explicit for the compiler).
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 }
 
 // Position of key-quad kq (keys 4kq..4kq+3 of a 32-key block) inside the
@@ -74,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int split = bid % a.S;
   const int b = bid / a.S;
 
-  const int L = min(a.cache_len[b], a.Lmax);
-  const int qp = a.q_pos[b];
+  const int L = __builtin_amdgcn_readfirstlane(min(a.cache_len[b], a.Lmax));
+  const int qp = __builtin_amdgcn_readfirstlane(a.q_pos[b]);
   const int ks0 = split * a.split_len;
   const int ks1 = min(L, ks0 + a.split_len);
 
@@ -90,10 +104,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       qr[p] = (n16 < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
   }
 
-  const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
-  const bf16* vbase = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
-  bf16* sv = sV[wave];
+  // K / V of this (sequence, kv head) through raw buffer resources that end
+  // after row L-1: rows past the cache length read as zero, and a lane whose
+  // 8 dims belong to a skipped group gets an out-of-range offset, so it
+  // fetches nothing and reads zero -- no branches around the loads.
+  const int krow_b = (int)(a.ks_t * 2);
+  const int vrow_b = (int)(a.vs_t * 2);
+  const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(
+      a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h, L > 0 ? (L - 1) * krow_b + 2 * D : 0);
+  const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(
+      a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h, L > 0 ? (L - 1) * vrow_b + 2 * D : 0);
+  constexpr int kOut = 0x7ffffff0;    // any offset >= the resource size
 
+  bf16* sv = sV[wave];
   float m_i = -INFINITY, l_i = 0.f;
   f32x4 o[ND];
 #pragma unroll
@@ -107,16 +130,56 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
   const float sl2 = a.scale_log2;
 
-  for (int jb = ks0 + 32 * wave; jb < ks1; jb += 32 * kWaves) {
+  struct Regs {
+    u32x4 k[2][NP];
+    u32x4 v[VITEMS][4];
+  };
+
+  // classes of the key block starting at jb: skip groups [0, sL), partial
+  // [sL, sR), full [sR, NG)
+  auto classify = [&](int jb, int& sL, int& sR) {
     const int jb1 = min(L, jb + 32) - 1;
     const int lD = qp - jb1;
     const int rD = qp - jb;
-    int sL = 0, sR = 0;
+    sL = 0;
+    sR = 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      sL += a.cut[g] < lD;
-      sR += a.cut[g] < rD;
+      sL = (a.cut[g] < lD) ? g + 1 : sL;
+      sR = (a.cut[g] < rD) ? g + 1 : sR;
     }
+    sL = __builtin_amdgcn_readfirstlane(sL);
+    sR = __builtin_amdgcn_readfirstlane(sR);
+  };
+
+  // issue every HBM load of one block: the kept K columns and all of V
+  auto load_block = [&](Regs& R, int jb) {
+    int sL, sR;
+    classify(jb, sL, sR);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int row = (jb + 16 * blk + n16) * krow_b;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int g = (32 * p + 8 * q4) / G;      // this lane's group in step p
+        const int off = (g >= sL) ? row + (32 * p + 8 * q4) * 2 : kOut;
+        R.k[blk][p] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int kq = lane & 7;
+      const int dc = (lane >> 3) + 8 * it;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        R.v[it][e] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (jb + 4 * kq + e) * vrow_b + dc * 16, 0, 0);
+    }
+  };
+
+  auto compute_block = [&](Regs& R, int jb) {
+    int sL, sR;
+    classify(jb, sL, sR);
+    const int jb1 = min(L, jb + 32) - 1;
     if (COUNT) {
       ++cnt_vis;
 #pragma unroll
@@ -126,33 +189,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         cnt[g][2] += (g >= sR);
       }
     }
-
-    // ---- issue every HBM load of this block: kept K columns, all of V ----
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 kr[2][NP];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int j = jb + 16 * blk + n16;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int g = (32 * p + 8 * q4) / G;      // this lane's group in step p
-        kr[blk][p] = (j <= jb1 && g >= sL)
-                         ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * a.ks_t + 32 * p + 8 * q4)
-                         : zero;
-      }
-    }
-    u32x4 vr[VITEMS][4];
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int kq = lane & 7;
-      const int dc = (lane >> 3) + 8 * it;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jb + 4 * kq + e;
-        vr[it][e] = (j <= jb1) ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * a.vs_t + dc * 8)
-                               : zero;
-      }
-    }
 
     // ---- S^T = K Q^T per 16-key block, group by group ----
     f32x4 s[2];
@@ -165,17 +202,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         const int g_hi = (32 * p + 31) / G;
         if (g_hi < sL) continue;                   // every lane skipped
         const int g = (32 * p + 8 * q4) / G;
+        if (g_lo >= sR) {                          // all full: skipped lanes read zero
+          s[blk] = mfma16(R.k[blk][p], qr[p], s[blk]);
+          continue;
+        }
         bool any_full = false;
 #pragma unroll
         for (int gg = g_lo; gg <= g_hi; ++gg) any_full |= (gg >= sR);
         if (any_full) {
-          const u32x4 op = (g >= sR) ? kr[blk][p] : zero;
+          const u32x4 op = (g >= sR) ? R.k[blk][p] : zero;
           s[blk] = mfma16(op, qr[p], s[blk]);
         }
 #pragma unroll
         for (int gg = g_lo; gg <= g_hi; ++gg) {
           if (gg < sL || gg >= sR) continue;       // only partial groups
-          const u32x4 op = (g == gg) ? kr[blk][p] : zero;
+          const u32x4 op = (g == gg) ? R.k[blk][p] : zero;
           const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
           const int cg = a.cut[gg];
 #pragma unroll
@@ -185,10 +226,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
           }
         }
       }
+      if (jb + 32 > L) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jb + 16 * blk + 4 * q4 + r;
-        if (j > jb1) s[blk][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int j = jb + 16 * blk + 4 * q4 + r;
+          if (j > jb1) s[blk][r] = -INFINITY;
+        }
       }
     }
 
@@ -200,12 +243,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const int pos = vt_pos32(kq);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const unsigned int w0 = vr[it][0][e], w1 = vr[it][1][e], w2 = vr[it][2][e], w3 = vr[it][3][e];
+        const unsigned int w0 = R.v[it][0][e], w1 = R.v[it][1][e], w2 = R.v[it][2][e], w3 = R.v[it][3][e];
         u32x2 even, odd;
-        even[0] = (w0 & 0xffffu) | (w1 << 16);
-        even[1] = (w2 & 0xffffu) | (w3 << 16);
-        odd[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        odd[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+        even[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // (w0.lo, w1.lo)
+        even[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+        odd[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);    // (w0.hi, w1.hi)
+        odd[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
         const int d = dc * 8 + 2 * e;
         *reinterpret_cast<u32x2*>(&sv[d * VS + pos]) = even;
         *reinterpret_cast<u32x2*>(&sv[(d + 1) * VS + pos]) = odd;
@@ -247,6 +290,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
     // the next block overwrites the tile only after these reads completed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // ---- this wave's blocks: jb = ks0 + 32*wave + 128*t; two register sets,
+  //      the next block's loads are in flight while one block computes ----
+  constexpr int kStride = 32 * kWaves;
+  Regs RA, RB;
+  int jb = ks0 + 32 * wave;
+  if (jb < ks1) load_block(RA, jb);
+  while (jb < ks1) {
+    const int jn = jb + kStride;
+    if (jn < ks1) load_block(RB, jn);
+    compute_block(RA, jb);
+    if (jn >= ks1) break;
+    const int jn2 = jn + kStride;
+    if (jn2 < ks1) load_block(RA, jn2);
+    compute_block(RB, jn);
+    jb = jn2;
   }
 
   // ---- merge the 4 waves of this split through LDS ----
