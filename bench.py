@@ -84,6 +84,40 @@ def decode_bytes(L, q_pos, Hkv, Hq, B, d_h, G, cut):
 
 
 # ---------------------------------------------------------------------------
+KERNEL_SOURCES = {
+    "prefill": ["rope_positional_encoding_amd/csrc/prefill.hip", "rope_positional_encoding_amd/csrc/wp_internal.h",
+                "rope_positional_encoding_amd/build.py"],
+    "decode": ["rope_positional_encoding_amd/csrc/decode.hip", "rope_positional_encoding_amd/csrc/wp_internal.h",
+               "rope_positional_encoding_amd/build.py"],
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    calibration) from profiles/traffic.txt, only if it was measured on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 4 and not line.startswith("#") and f[0] == kernel:
+            if f[1] != source_hash(kernel):
+                return None
+            return float(f[2]) + float(f[3])
+    return None
+
+
+# ---------------------------------------------------------------------------
 def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512):
     """The CPU oracle (as it stands) on seeded uniform query rows of the same
     32K prefill (the rotated inputs the GPU consumed), single BLAS thread;
@@ -227,6 +261,7 @@ def main():
     dense_f, alg_f, exe_f = prefill_flops(n, Hq, 1, d, G, cut)
     kv_dense, dec_alg, dec_issued = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G, cut)
     rope_bytes = 2 * 2.0 * (q_raw.numel() + k_raw.numel())
+    prefill_bytes = 2.0 * (2 * q_raw.numel() + 2 * k_raw.numel())   # read q, k, v; write o
 
     out = {
         "metric": METRIC,
@@ -276,11 +311,13 @@ def main():
     # over the average launch duration measured with events on its stream
     ach = alg_f / (avg["prefill"] * 1e-3) / 1e12
     out["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                       "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                       "traffic": measured_traffic("prefill"), "algorithmic_bytes": prefill_bytes,
                        "kernel": "prefill_kernel<128,16>", "avg_ms": round(avg["prefill"], 4)}
     ach_d = dec_alg / (avg["decode"] * 1e-3) / 1e9
     out["roofline_decode"] = {"bound": "hbm", "achieved": round(ach_d, 1), "peak": PEAK_HBM_GBS,
-                              "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4), "traffic": None,
+                              "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
+                              "traffic": measured_traffic("decode"), "algorithmic_bytes": dec_alg,
                               "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
                               "avg_ms": round(avg["decode"], 4)}
     if not args.no_cpu_baseline:
