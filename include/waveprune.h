@@ -123,7 +123,10 @@ wp_status wp_rope_apply(const void* x, int32_t x_dtype, void* y,
  * (0 skip, 1 partial, 2 full), summed over batches and query heads, and
  * counters[3*(d_h/G)] the number of visited tiles.  Counts are added; the
  * caller zeroes the buffer.  May be NULL otherwise.
- * n >= 1, B >= 1, Hkv >= 1, Hq % Hkv == 0.
+ * n >= 1, B >= 1, Hkv >= 1, Hq % Hkv == 0.  The k and v token strides must be
+ * >= d_h, and (n-1) * token_stride + d_h elements of one sequence must span
+ * less than 2^31 bytes (K/V are read through 32-bit-addressed buffer
+ * resources); otherwise WP_ERR_SHAPE.
  */
 wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                      int32_t B, int32_t n, int32_t Hq, int32_t Hkv, int32_t d_h,
@@ -150,6 +153,8 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
  * 256-byte aligned, used for the per-split partial results.
  * counters (WP_FLAG_COUNT): device int64[3*(d_h/G)+1], as in wp_prefill but
  * counted per (sequence, kv head, key block).
+ * The cache token strides must be >= d_h and one sequence of the cache must
+ * span less than 2^31 bytes (WP_ERR_SHAPE otherwise).
  */
 wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                     const int32_t* cache_len, const int32_t* q_pos,

@@ -218,6 +218,13 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
   if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
     return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
   if (wp_status s = check_strides(strides, 12)) return s;
+  // K/V rows are fetched through buffer resources: rows must not overlap and
+  // one sequence's rows must span less than 2^31 bytes
+  if (strides[4] < d_h || strides[7] < d_h)
+    return fail(WP_ERR_SHAPE, "k/v token strides must be >= d_h");
+  if ((int64_t)(n - 1) * strides[4] * 2 + 2 * d_h >= 2147483647LL ||
+      (int64_t)(n - 1) * strides[7] * 2 + 2 * d_h >= 2147483647LL)
+    return fail(WP_ERR_SHAPE, "one sequence of K or V spans 2^31 bytes or more");
   const int ng = d_h / G;
   wp::PrefillArgs a;
   memset(&a, 0, sizeof(a));
@@ -310,6 +317,11 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
   if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
     return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
   if (wp_status s = check_strides(strides, 10)) return s;
+  if (strides[3] < d_h || strides[6] < d_h)
+    return fail(WP_ERR_SHAPE, "k/v cache token strides must be >= d_h");
+  if ((int64_t)(Lmax - 1) * strides[3] * 2 + 2 * d_h >= 2147483647LL ||
+      (int64_t)(Lmax - 1) * strides[6] * 2 + 2 * d_h >= 2147483647LL)
+    return fail(WP_ERR_SHAPE, "one sequence of the K or V cache spans 2^31 bytes or more");
   const size_t need = wp_decode_workspace_size(B, Lmax, Hq, Hkv, d_h, num_splits);
   if (workspace_bytes < need)
     return fail(WP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);

@@ -26,12 +26,16 @@
 //  * A workgroup is 4 waves that share one kv head and one key range: with
 //    GQA ratio >= 4 the waves are 4 query heads over the same 32 queries
 //    (identical tile classes, K/V staged once in LDS for all four).
-//  * K is staged row-major in LDS (row pad 16 B: conflict-free 16-byte MFMA
-//    operand reads); V is written transposed (V^T) with a key permutation
-//    that matches the S^T register layout, so both MFMA operands of P.V are
-//    single 16-byte LDS reads.  LDS holds two stages: while tile t is
-//    consumed, tile t+1 is written into the other stage and tile t+2 is in
-//    flight from HBM into registers; one barrier per tile.
+//  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ...
+//    lds: no register staging, rows past the sequence end arrive as zeros).
+//    Both are stored row-major with an XOR swizzle of their 16-byte chunks:
+//    K by (row & 7), so the 16-byte MFMA operand reads of 8 consecutive rows
+//    hit distinct banks; V by (row & 3), so the transposing reads
+//    (ds_read_b64_tr_b16) of 4 rows hit distinct banks.  A V^T operand of
+//    the P.V MFMA is two transposing reads: each returns, to a lane, 4
+//    consecutive keys at one head dim -- exactly the two runs of 4 keys
+//    that the lane's S^T registers hold.  Two LDS stages: tile t+1 streams
+//    in while tile t is consumed; one barrier per tile.
 //  * The running max is refreshed (and O rescaled) only when it grows by more
 //    than 8 in log2 units, so every probability stays below 2^8; the final
 //    O / l and the LSE are unaffected.
@@ -45,9 +49,26 @@ namespace wp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 // dword 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kTileKeys = 64;     // keys per tile: two 32-key MFMA blocks, one class per group
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// The LDS address-space casts live in device-only helpers: the kernel body
+// must stay valid for the host compilation pass that emits its launch stub.
+// 16 bytes per lane from a raw buffer straight into LDS at dst + 16*lane.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voffset, 0, 0, 0);
+}
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
+// of the 4 x 16-bit values addressed by lanes 4e + i / 4, e = 0..3.
+__device__ inline u32x2 read_tr16(const void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
 
 __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -89,34 +110,22 @@ __device__ inline float halves_sum(float x) {
 // Row (key) of register r of a 32x32 MFMA output block for lane half hh.
 __device__ inline int out_row(int r, int hh) { return ((r >> 2) << 3) + (hh << 2) + (r & 3); }
 
-// Position of key-quad kq (keys 4kq..4kq+3 of a 64-key tile) in the
-// transposed V tile: inside each 16-key chunk the 4-key blocks are stored in
-// the order 0, 2, 1, 3, so that lane half hh of an MFMA operand reads the
-// keys {4hh..4hh+3, 8+4hh..8+4hh+3} -- the keys its S^T registers hold -- as
-// one contiguous 16-byte run.
-__device__ inline int vt_pos(int kq) {
-  const int blk = kq & 3;
-  const int nb = (blk == 1) ? 2 : (blk == 2) ? 1 : blk;
-  return ((kq >> 2) << 4) + (nb << 2);
-}
-
 template <int D, int G, bool COUNT>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int NCH = D / 16;         // 16-dim MFMA steps
   constexpr int GC = G / 16;          // MFMA steps per group
   constexpr int NG = D / G;           // groups
   constexpr int ND = D / 32;          // 32-dim output blocks
-  constexpr int KS = D + 8;           // K row stride in LDS (elements)
-  constexpr int VS = kTileKeys + 8;   // V^T row stride in LDS (elements)
-  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int KITEMS = kTileKeys * CPR / kThreads;   // K chunks per thread
-  constexpr int VITEMS = 16 * CPR;                     // (key quad, chunk) items
-  static_assert(KITEMS >= 1 && VITEMS <= kThreads, "tile shape");
+  constexpr int RB = D * 2;           // bytes per K/V row in LDS (no padding)
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int TILE_B = kTileKeys * RB;                 // bytes per K (or V) tile
+  constexpr int LOADS = TILE_B / (kWaves * 64 * 16);     // DMA loads per wave per tile
+  constexpr int VX = CPR / 4;          // V swizzle unit: chunk ^= (row & 3) * VX
+  static_assert(LOADS >= 1 && (TILE_B % (kWaves * 64 * 16)) == 0, "tile shape");
 
-  // two LDS stages: tile t is consumed from stage t&1 while tile t+1 is
-  // written into the other one
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][kTileKeys * KS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][D * VS];
+  // LDS: [stage][K tile | V tile]; tile t is read from stage t&1 while tile
+  // t+1 streams into the other stage
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,6 +153,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
   const bf16* vbase = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
+  const int krow_b = (int)(a.ks_t * 2);     // bytes between consecutive keys in HBM
+  const int vrow_b = (int)(a.vs_t * 2);
 
   // Q^T operand, resident for the whole kernel: lane owns query i0w + l32,
   // dims [16c + 8hh, 16c + 8hh + 8) of MFMA step c.
@@ -157,69 +168,55 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       qr[c] = (i < n) ? *reinterpret_cast<const u32x4*>(qp + c * 16) : zero;
   }
 
-  // register staging of the next K/V tile.  Tile rows are fetched with raw
-  // buffer loads whose resource starts at the tile's first row and ends
-  // after row n-1: rows past the end of the sequence read as zero, and the
-  // per-thread byte offsets are loop invariant.
-  u32x4 kreg[KITEMS];
-  u32x4 vreg[4];
-  const int v_kq = tid & 15;
-  const int v_dc = tid >> 4;
-  const bool v_active = tid < VITEMS;
-  const int krow_b = (int)(a.ks_t * 2);     // bytes between consecutive keys
-  const int vrow_b = (int)(a.vs_t * 2);
-  int koff[KITEMS];
+  // ---- DMA of one tile into LDS.  Load i of this wave fills LDS chunks
+  //      p = (wave*LOADS + i)*64 + lane (16 bytes each); chunk p holds row
+  //      p / CPR, logical chunk (p % CPR) ^ swizzle(row). ----
+  int koff[LOADS], voff[LOADS];
 #pragma unroll
-  for (int it = 0; it < KITEMS; ++it) {
-    const int idx = tid + it * kThreads;
-    koff[it] = (idx / CPR) * krow_b + (idx % CPR) * 16;
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = (wave * LOADS + i) * 64 + lane;
+    const int row = p / CPR;
+    const int pc = p % CPR;
+    koff[i] = row * krow_b + (pc ^ (row & 7)) * 16;
+    voff[i] = row * vrow_b + (pc ^ ((row & 3) * VX)) * 16;
   }
-  const int voff = 4 * v_kq * vrow_b + v_dc * 16;
-
-  auto load_tile = [&](int j0) {
+  auto load_tile = [&](int j0, int stage) {
     const int rows = n - j0;                                  // >= 1
     const __amdgpu_buffer_rsrc_t kr =
         uniform_rsrc(kbase + (int64_t)j0 * a.ks_t, (rows - 1) * krow_b + 2 * D);
     const __amdgpu_buffer_rsrc_t vr =
         uniform_rsrc(vbase + (int64_t)j0 * a.vs_t, (rows - 1) * vrow_b + 2 * D);
+    unsigned char* kdst = &smem[stage][0];
+    unsigned char* vdst = &smem[stage][TILE_B];
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it)
-      kreg[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[it], 0, 0);
-    if (v_active) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        vreg[q4] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + q4 * vrow_b, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+      const int dst = (wave * LOADS + i) * 1024;
+      dma16(kr, kdst + dst, koff[i]);
+      dma16(vr, vdst + dst, voff[i]);
     }
   };
 
-  auto store_tile = [&](int stage) {
-    bf16* k_s = sK[stage];
-    bf16* v_s = sV[stage];
+  // ---- per-lane LDS read offsets (bytes, relative to a stage) ----
+  // K operand of S^T: lane reads row 32kb + l32, logical chunk 2s + hh of
+  // MFMA step s; physical chunk (2s + hh) ^ (l32 & 7).  Steps s and s + 4
+  // differ only in chunk bit 3, which the swizzle leaves alone: +128 bytes.
+  const int xk = l32 & 7;
+  int kread[4];
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int idx = tid + it * kThreads;
-      const int key = idx / CPR;
-      const int dc = idx % CPR;
-      *reinterpret_cast<u32x4*>(&k_s[key * KS + dc * 8]) = kreg[it];
-    }
-    if (v_active) {
-      // vreg[q] holds dims [8dc, 8dc+8) of key 4kq+q as 4 dwords of 2 dims;
-      // write, for every dim, the 4 keys as one 8-byte run of V^T.
-      const int pos = vt_pos(v_kq);
+  for (int s4 = 0; s4 < 4; ++s4) kread[s4] = l32 * RB + (((2 * s4 + hh) ^ xk) & 7) * 16;
+  // V^T operand of P.V via two transposing reads.  In a 16-lane group, lane
+  // j = 4e + q reads 4 dims [D0 + 4q, D0 + 4q + 4) of key row K0 + e; lane i
+  // then holds keys K0..K0+3 at dim D0 + i.  Here D0 = 32db + 16*(group&1),
+  // K0 = 16kc + 4hh (+ 8 for the second read).
+  const int grp = lane >> 4;
+  const int e4 = (lane & 15) >> 2;
+  const int q4 = lane & 3;
+  int vread[ND];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned int w0 = vreg[0][e], w1 = vreg[1][e], w2 = vreg[2][e], w3 = vreg[3][e];
-        u32x2 even, odd;
-        even[0] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // (w0.lo, w1.lo)
-        even[1] = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-        odd[0] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);    // (w0.hi, w1.hi)
-        odd[1] = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-        const int d = v_dc * 8 + 2 * e;
-        *reinterpret_cast<u32x2*>(&v_s[d * VS + pos]) = even;
-        *reinterpret_cast<u32x2*>(&v_s[(d + 1) * VS + pos]) = odd;
-      }
-    }
-  };
+  for (int db = 0; db < ND; ++db) {
+    const int chunk = 4 * db + 2 * (grp & 1) + (q4 >> 1);
+    vread[db] = (4 * hh + e4) * RB + (chunk ^ (e4 * VX)) * 16 + (q4 & 1) * 8;
+  }
 
   float m_i = -INFINITY;   // running max (log2 domain), possibly stale by < 8
   float l_i = 0.f;         // running sum (this lane's half of the keys)
@@ -239,14 +236,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const float sl2 = a.scale_log2;
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
-  store_tile(0);
-  if (nk > 1) load_tile(kTileKeys);
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int it = 0; it < nk; ++it) {
     const int j0 = it * kTileKeys;
     const int stage = it & 1;
+    if (it + 1 < nk) load_tile(j0 + kTileKeys, stage ^ 1);
+    const unsigned char* sk = &smem[stage][0];
+    const unsigned char* sv = &smem[stage][TILE_B];
     if (wave_valid && j0 <= i1w) {
       // ---- classify the (32 queries x 64 keys) tile ----
       const int j1 = min(n - 1, j0 + kTileKeys - 1);
@@ -271,19 +270,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
 
+      // K operand of MFMA step c for key block kb
+      auto kop = [&](int kb, int c) {
+        return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c & 3] + (c >> 2) * 128);
+      };
+
       // ---- S^T = K Q^T: full groups [sR, NG) as one chain, highest first ----
-      const bf16* k0 = &sK[stage][l32 * KS + hh * 8];
-      const bf16* k1 = k0 + 32 * KS;
       f32x16 s0, s1;
       if (sR < NG) {
         {
           constexpr int c0 = (NG - 1) * GC;
-          s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + c0 * 16), qr[c0], zero16);
-          s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + c0 * 16), qr[c0], zero16);
+          s0 = mfma32(kop(0, c0), qr[c0], zero16);
+          s1 = mfma32(kop(1, c0), qr[c0], zero16);
 #pragma unroll
           for (int c = 1; c < GC; ++c) {
-            s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + (c0 + c) * 16), qr[c0 + c], s0);
-            s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + (c0 + c) * 16), qr[c0 + c], s1);
+            s0 = mfma32(kop(0, c0 + c), qr[c0 + c], s0);
+            s1 = mfma32(kop(1, c0 + c), qr[c0 + c], s1);
           }
         }
 #pragma unroll
@@ -292,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int c = 0; c < GC; ++c) {
             const int cc = g * GC + c;
-            s0 = mfma32(*reinterpret_cast<const u32x4*>(k0 + cc * 16), qr[cc], s0);
-            s1 = mfma32(*reinterpret_cast<const u32x4*>(k1 + cc * 16), qr[cc], s1);
+            s0 = mfma32(kop(0, cc), qr[cc], s0);
+            s1 = mfma32(kop(1, cc), qr[cc], s1);
           }
         }
       } else {
@@ -310,18 +312,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
           const int cg = a.cut[g];
           f32x16 t = zero16;
 #pragma unroll
-          for (int c = 0; c < GC; ++c) {
-            const int cc = g * GC + c;
-            t = mfma32(*reinterpret_cast<const u32x4*>(k0 + cc * 16), qr[cc], t);
-          }
+          for (int c = 0; c < GC; ++c) t = mfma32(kop(0, g * GC + c), qr[g * GC + c], t);
 #pragma unroll
           for (int r = 0; r < 16; ++r) s0[r] += (base - out_row(r, hh) <= cg) ? t[r] : 0.f;
           t = zero16;
 #pragma unroll
-          for (int c = 0; c < GC; ++c) {
-            const int cc = g * GC + c;
-            t = mfma32(*reinterpret_cast<const u32x4*>(k1 + cc * 16), qr[cc], t);
-          }
+          for (int c = 0; c < GC; ++c) t = mfma32(kop(1, g * GC + c), qr[g * GC + c], t);
 #pragma unroll
           for (int r = 0; r < 16; ++r) s1[r] += (base - 32 - out_row(r, hh) <= cg) ? t[r] : 0.f;
         }
@@ -370,20 +366,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
           p[2 + c][w] = pack_bf16x2(f0, f1);
         }
 
-      // ---- O^T += V^T P^T ----
-      const bf16* vs = &sV[stage][l32 * VS + hh * 8];
+      // ---- O^T += V^T P^T; the V^T operand is two transposing reads ----
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const u32x4 va = *reinterpret_cast<const u32x4*>(vs + db * 32 * VS + kc * 16);
-          o[db] = mfma32(va, p[kc], o[db]);
+          const unsigned char* va = sv + kc * 16 * RB + vread[db];
+          const u32x2 lo2 = read_tr16(va);
+          const u32x2 hi2 = read_tr16(va + 8 * RB);
+          const u32x4 vop = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          o[db] = mfma32(vop, p[kc], o[db]);
         }
     }
 
-    // ---- stage the next tile; prefetch the one after ----
-    if (it + 1 < nk) store_tile(stage ^ 1);
-    if (it + 2 < nk) load_tile((it + 2) * kTileKeys);
+    // tile it+1 must be in LDS, and every wave done with stage it&1, before
+    // the next iteration
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 

@@ -103,7 +103,8 @@ FAKE = ctypes.c_void_p(0x7F0000000000)   # never dereferenced: every call below 
 
 
 def _strides(n):
-    return (ctypes.c_int64 * n)(*([8] * n))
+    # plausible element strides (multiples of 8, token strides >= d_h = 128)
+    return (ctypes.c_int64 * n)(*([1024] * n))
 
 
 def _prefill(**kw):
@@ -129,6 +130,12 @@ def test_prefill_validation_codes():
     assert _prefill(cut=None) == -1
     assert _prefill(flags=2) == -1                       # COUNT without counters
     assert _prefill(flags=8) == -6                       # unknown flag
+    st = _strides(12)
+    st[4] = 64                                           # k token stride < d_h
+    assert _prefill(strides=st) == -2
+    st = _strides(12)
+    st[7] = 1 << 24                                      # one V sequence > 2 GiB
+    assert _prefill(strides=st, n=200) == -2
 
 
 def _decode(**kw):
