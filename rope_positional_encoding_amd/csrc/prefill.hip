@@ -28,10 +28,13 @@
 //    (identical tile classes, K/V staged once in LDS for all four).
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ...
 //    lds: no register staging, rows past the sequence end arrive as zeros).
-//    Both are stored row-major with an XOR swizzle of their 16-byte chunks:
-//    K by (row & 7), so the 16-byte MFMA operand reads of 8 consecutive rows
-//    hit distinct banks; V by (row & 3), so the transposing reads
-//    (ds_read_b64_tr_b16) of 4 rows hit distinct banks.  A V^T operand of
+//    Both are stored row-major with an XOR swizzle of their 16-byte chunks.
+//    LDS has 64 banks of 4 bytes (one 256-byte bank row) and serves 16 lanes
+//    of a 16-byte read at a time, so K is swizzled by the index of the row's
+//    bank row (row for d_h = 128, row / 2 for d_h = 64): the MFMA operand
+//    reads of 16 consecutive rows then hit all 64 banks once.  V is swizzled
+//    by (row & 3), so the transposing reads (ds_read_b64_tr_b16) of 4 rows
+//    hit distinct banks.  A V^T operand of
 //    the P.V MFMA is two transposing reads: each returns, to a lane, 4
 //    consecutive keys at one head dim -- exactly the two runs of 4 keys
 //    that the lane's S^T registers hold.  Two LDS stages: tile t+1 streams
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int TILE_B = kTileKeys * RB;                 // bytes per K (or V) tile
   constexpr int LOADS = TILE_B / (kWaves * 64 * 16);     // DMA loads per wave per tile
   constexpr int VX = CPR / 4;          // V swizzle unit: chunk ^= (row & 3) * VX
+  constexpr int KRB = 256 / RB;        // K rows per 256-byte LDS bank row
   static_assert(LOADS >= 1 && (TILE_B % (kWaves * 64 * 16)) == 0, "tile shape");
 
   // LDS: [stage][K tile | V tile]; tile t is read from stage t&1 while tile
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int p = (wave * LOADS + i) * 64 + lane;
     const int row = p / CPR;
     const int pc = p % CPR;
-    koff[i] = row * krow_b + (pc ^ (row & 7)) * 16;
+    koff[i] = row * krow_b + (pc ^ ((row / KRB) & (CPR - 1))) * 16;
     voff[i] = row * vrow_b + (pc ^ ((row & 3) * VX)) * 16;
   }
   auto load_tile = [&](int j0, int stage) {
@@ -198,12 +202,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   // ---- per-lane LDS read offsets (bytes, relative to a stage) ----
   // K operand of S^T: lane reads row 32kb + l32, logical chunk 2s + hh of
-  // MFMA step s; physical chunk (2s + hh) ^ (l32 & 7).  Steps s and s + 4
-  // differ only in chunk bit 3, which the swizzle leaves alone: +128 bytes.
-  const int xk = l32 & 7;
-  int kread[4];
+  // MFMA step s; physical chunk (2s + hh) ^ swizzle(l32) (the swizzle of
+  // rows 32kb + l32 does not depend on kb).
+  const int xk = (l32 / KRB) & (CPR - 1);
+  int kread[NCH];
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) kread[s4] = l32 * RB + (((2 * s4 + hh) ^ xk) & 7) * 16;
+  for (int c = 0; c < NCH; ++c) kread[c] = l32 * RB + ((2 * c + hh) ^ xk) * 16;
   // V^T operand of P.V via two transposing reads.  In a 16-lane group, lane
   // j = 4e + q reads 4 dims [D0 + 4q, D0 + 4q + 4) of key row K0 + e; lane i
   // then holds keys K0..K0+3 at dim D0 + i.  Here D0 = 32db + 16*(group&1),
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
       // K operand of MFMA step c for key block kb
       auto kop = [&](int kb, int c) {
-        return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c & 3] + (c >> 2) * 128);
+        return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c]);
       };
 
       // ---- S^T = K Q^T: full groups [sR, NG) as one chain, highest first ----
