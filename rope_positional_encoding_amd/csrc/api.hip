@@ -247,13 +247,13 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
   a.B = B; a.n = n; a.Hq = Hq; a.Hkv = Hkv;
   a.r = Hq / Hkv;
   a.HPW = (a.r % 4 == 0) ? 4 : (a.r % 2 == 0 ? 2 : 1);
-  a.QSUB = 4 / a.HPW;
   a.HG = a.r / a.HPW;
-  a.QB = 32 * a.QSUB;
-  a.nqb = (n + a.QB - 1) / a.QB;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
-  const long long blocks = (long long)B * Hkv * a.HG * a.nqb;
-  if (blocks > 2147483647LL) return fail(WP_ERR_SHAPE, "grid too large");
+  // the query sub-blocks per workgroup (QSUB, QB, nqb) follow from the
+  // kernel's wave count and are set by launch_prefill; 32 queries per wave
+  // is the smallest workgroup, so this bounds every grid
+  const long long max_blocks = (long long)B * Hkv * a.HG * ((n + 31) / 32);
+  if (max_blocks > 2147483647LL) return fail(WP_ERR_SHAPE, "grid too large");
   hipError_t e = wp::launch_prefill(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();

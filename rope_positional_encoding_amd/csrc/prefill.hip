@@ -23,9 +23,11 @@
 //    own accumulator, is masked with dist <= cutoff, then added, on a
 //    separate path that only boundary tiles take.  No per-(splitL, splitR)
 //    code specialization is needed.
-//  * A workgroup is 4 waves that share one kv head and one key range: with
-//    GQA ratio >= 4 the waves are 4 query heads over the same 32 queries
-//    (identical tile classes, K/V staged once in LDS for all four).
+//  * A workgroup is 8 waves (2 per SIMD, one workgroup per CU) that share
+//    one kv head and one key range: with GQA ratio >= 4 the waves are 4
+//    query heads x 2 blocks of 32 queries, so every K/V tile staged in LDS
+//    feeds 256 query rows.  Waves of one query block have identical tile
+//    classes.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ...
 //    lds: no register staging, rows past the sequence end arrive as zeros).
 //    Both are stored row-major with an XOR swizzle of their 16-byte chunks.
@@ -51,8 +53,8 @@ namespace wp {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 // dword 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kTileKeys = 64;     // keys per tile: two 32-key MFMA blocks, one class per group
@@ -71,6 +73,26 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voffset) {
 // of the 4 x 16-bit values addressed by lanes 4e + i / 4, e = 0..3.
 __device__ inline u32x2 read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// The two K operands (key blocks 0 and 1) of one S^T step, complete on
+// return.  Written as one asm block with its own wait so that the compiler
+// keeps it where it is placed (after the previous step's MFMAs) instead of
+// sinking the reads next to their first use.
+template <int OFF>
+__device__ inline void k_reads(u32x4& a, u32x4& b, unsigned addr) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "n"(OFF)
+      : "memory");
 }
 
 __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -114,7 +136,7 @@ __device__ inline float halves_sum(float x) {
 __device__ inline int out_row(int r, int hh) { return ((r >> 2) << 3) + (hh << 2) + (r & 3); }
 
 template <int D, int G, bool COUNT>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int NCH = D / 16;         // 16-dim MFMA steps
   constexpr int GC = G / 16;          // MFMA steps per group
   constexpr int NG = D / G;           // groups
@@ -279,32 +301,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c]);
       };
 
-      // ---- S^T = K Q^T: full groups [sR, NG) as one chain, highest first ----
-      f32x16 s0, s1;
+      // ---- S^T = K Q^T: full groups [sR, NG) as one chain of MFMA steps
+      //      from the highest down to step sR * GC.  The K operands of step
+      //      c-1 are read right after the MFMAs of step c are issued, so the
+      //      LDS latency overlaps their execution. ----
+      f32x16 s0 = zero16, s1 = zero16;
       if (sR < NG) {
-        {
-          constexpr int c0 = (NG - 1) * GC;
-          s0 = mfma32(kop(0, c0), qr[c0], zero16);
-          s1 = mfma32(kop(1, c0), qr[c0], zero16);
+        const int c_end = sR * GC;
+        const unsigned skb = lds_addr(sk);
+        u32x4 ka0, ka1;
+        k_reads<32 * RB>(ka0, ka1, skb + kread[NCH - 1]);
 #pragma unroll
-          for (int c = 1; c < GC; ++c) {
-            s0 = mfma32(kop(0, c0 + c), qr[c0 + c], s0);
-            s1 = mfma32(kop(1, c0 + c), qr[c0 + c], s1);
-          }
+        for (int cc = NCH - 1; cc >= 0; --cc) {
+          s0 = mfma32(ka0, qr[cc], cc == NCH - 1 ? zero16 : s0);
+          s1 = mfma32(ka1, qr[cc], cc == NCH - 1 ? zero16 : s1);
+          if (cc == c_end) break;
+          __builtin_amdgcn_sched_barrier(0);
+          k_reads<32 * RB>(ka0, ka1, skb + kread[cc - 1]);
         }
-#pragma unroll
-        for (int g = NG - 2; g >= 0; --g) {
-          if (g < sR) break;
-#pragma unroll
-          for (int c = 0; c < GC; ++c) {
-            const int cc = g * GC + c;
-            s0 = mfma32(kop(0, cc), qr[cc], s0);
-            s1 = mfma32(kop(1, cc), qr[cc], s1);
-          }
-        }
-      } else {
-        s0 = zero16;
-        s1 = zero16;
       }
 
       // ---- partial groups [sL, sR): compute, mask dist <= cutoff, add ----
@@ -419,7 +433,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_dg(const PrefillArgs& a, bool count, hipStream_t s) {
+hipError_t launch_dg(const PrefillArgs& a0, bool count, hipStream_t s) {
+  // each wave takes 32 queries of one head: HPW heads x QSUB query blocks
+  PrefillArgs a = a0;
+  a.QSUB = kWaves / a.HPW;
+  a.QB = 32 * a.QSUB;
+  a.nqb = (a.n + a.QB - 1) / a.QB;
   const long long blocks = (long long)a.B * a.Hkv * a.HG * a.nqb;
   if (blocks <= 0) return hipSuccess;
   if (count)

@@ -51,10 +51,10 @@ struct PrefillArgs {
   int B, n, Hq, Hkv;
   int r;        // Hq / Hkv
   int HPW;      // query heads per workgroup
-  int QSUB;     // 32-query sub-blocks per workgroup (4 / HPW)
+  int QSUB;     // 32-query sub-blocks per workgroup (waves / HPW; set by launch_prefill)
   int HG;       // head groups per kv head (r / HPW)
-  int QB;       // queries per workgroup (32 * QSUB)
-  int nqb;      // query blocks of QB
+  int QB;       // queries per workgroup (32 * QSUB; set by launch_prefill)
+  int nqb;      // query blocks of QB (set by launch_prefill)
   float scale_log2;   // log2(e) / sqrt(d_h)
   int cut[kMaxGroups];
 };
