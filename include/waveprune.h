@@ -147,8 +147,10 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
  * Same rule as wp_prefill; per key block of BN keys (wp_decode_tiling) the K
  * dims of skipped groups are not read ([notes] section 2.3: skipped groups
  * read no K cache).
- * The key range is split into num_splits chunks (0 = automatic, see
- * wp_decode_num_splits) computed independently, then merged.
+ * The key blocks are dealt to num_splits splits (0 = automatic, see
+ * wp_decode_num_splits; at most one split per key block): split s takes
+ * blocks s, s + S, s + 2S, ...  Splits are computed independently, then
+ * merged.
  * workspace: device memory of at least wp_decode_workspace_size(...) bytes,
  * 256-byte aligned, used for the per-split partial results.
  * counters (WP_FLAG_COUNT): device int64[3*(d_h/G)+1], as in wp_prefill but
@@ -163,7 +165,9 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     uint32_t flags, int64_t* counters, void* stream);
 
-/* Number of key splits wp_decode uses when num_splits == 0. */
+/* Number of key splits wp_decode uses when num_splits == 0: the count that
+ * spreads B * Hkv * splits workgroups over the current device's compute
+ * units with the fewest keys per unit (at least 128 keys per split). */
 int32_t wp_decode_num_splits(int32_t B, int32_t Lmax, int32_t Hkv);
 
 /* Workspace bytes wp_decode needs for these sizes (num_splits 0 = automatic). */

@@ -259,25 +259,47 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
   return ok();
 }
 
+namespace {
+// compute units of the current device (256 on MI355X; fewer in a partition)
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+}  // namespace
+
 int32_t wp_decode_num_splits(int32_t B, int32_t Lmax, int32_t Hkv) {
   if (B < 1 || Hkv < 1 || Lmax < 1) return 1;
+  // A decode workgroup fills one CU, and every split of a (sequence, kv
+  // head) does the same work, so the kernel takes about
+  // ceil(units * S / CUs) rounds of L / S keys: pick the S with the fewest
+  // keys per CU (the smallest such S), at least 128 keys per split.
   const long long units = (long long)B * Hkv;
-  long long s = (2048 + units - 1) / units;                 // about 2048 workgroups
-  const long long max_s = ((long long)Lmax + 127) / 128;    // at least 128 keys per split
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return (int32_t)s;
+  const long long cus = device_cus();
+  long long max_s = ((long long)Lmax + 127) / 128;
+  if (max_s > 4 * cus) max_s = 4 * cus;
+  long long best = 1;
+  double best_cost = (double)((units + cus - 1) / cus);
+  for (long long s = 2; s <= max_s; ++s) {
+    const double cost = (double)((units * s + cus - 1) / cus) / (double)s;
+    if (cost < best_cost * (1.0 - 1e-9)) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return (int32_t)best;
 }
 
 namespace {
-// split geometry: split_len is a multiple of the decode key block
-void decode_geometry(int32_t B, int32_t Lmax, int32_t Hkv, int32_t num_splits, int* S, int* split_len) {
-  int s = num_splits > 0 ? num_splits : wp_decode_num_splits(B, Lmax, Hkv);
-  long long len = ((long long)Lmax + s - 1) / s;
-  len = ((len + wp::kDecodeBN - 1) / wp::kDecodeBN) * wp::kDecodeBN;
-  if (len < wp::kDecodeBN) len = wp::kDecodeBN;
-  *split_len = (int)len;
-  *S = (int)(((long long)Lmax + len - 1) / len);
+// number of splits: the requested (or automatic) count, at most one per
+// key block of the cache
+int decode_splits(int32_t B, int32_t Lmax, int32_t Hkv, int32_t num_splits) {
+  long long s = num_splits > 0 ? num_splits : wp_decode_num_splits(B, Lmax, Hkv);
+  const long long blocks = ((long long)Lmax + wp::kDecodeBN - 1) / wp::kDecodeBN;
+  if (s > blocks) s = blocks;
+  return (int)(s < 1 ? 1 : s);
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
@@ -285,8 +307,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t wp_decode_workspace_size(int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv, int32_t d_h,
                                 int32_t num_splits) {
   if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d_h < 1) return 0;
-  int S, len;
-  decode_geometry(B, Lmax, Hkv, num_splits, &S, &len);
+  const int S = decode_splits(B, Lmax, Hkv, num_splits);
   const size_t rows = (size_t)B * Hq * S;
   return align256(rows * d_h * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
@@ -334,8 +355,7 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
     if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
     for (int g = 0; g < ng; ++g) a.cut[g] = cutoffs[g];
   }
-  int S, split_len;
-  decode_geometry(B, Lmax, Hkv, num_splits, &S, &split_len);
+  const int S = decode_splits(B, Lmax, Hkv, num_splits);
   const size_t rows = (size_t)B * Hq * S;
   a.q = static_cast<const wp::bf16*>(q);
   a.k = static_cast<const wp::bf16*>(k_cache);
@@ -353,7 +373,6 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
   a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv;
   a.r = Hq / Hkv;
   a.S = S;
-  a.split_len = split_len;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
   const long long blocks = (long long)B * Hkv * S;
   if (blocks > 2147483647LL || (long long)B * Hq > 2147483647LL)

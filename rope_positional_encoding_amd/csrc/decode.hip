@@ -10,9 +10,11 @@
 //
 // gfx950 design:
 //  * HBM-bound: the aim is to stream the kept K bytes and all V bytes once.
-//    A workgroup (4 waves) owns one (sequence, kv head, key split); each wave
-//    walks its own 32-key blocks of the split independently (no barriers in
-//    the loop) and keeps its own online-softmax state for the GQA heads.
+//    A workgroup (4 waves) owns one (sequence, kv head, split); split s of S
+//    takes the 32-key blocks s, s + S, s + 2S, ... so that all splits of a
+//    sequence advance through the cache together.  Each wave walks its own
+//    blocks independently (no barriers in the loop) and keeps its own
+//    online-softmax state for the GQA heads.
 //  * QK on v_mfma_f32_16x16x32_bf16 with the keys as rows: each lane loads
 //    16 contiguous bytes of one key row straight from HBM into the MFMA A
 //    operand; the GQA heads (<= 16) are the B columns, held in registers.
@@ -90,8 +92,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   const int L = __builtin_amdgcn_readfirstlane(min(a.cache_len[b], a.Lmax));
   const int qp = __builtin_amdgcn_readfirstlane(a.q_pos[b]);
-  const int ks0 = split * a.split_len;
-  const int ks1 = min(L, ks0 + a.split_len);
 
   // Q^T operand: column n16 = head kvh*r + n16 (zero beyond r), dims
   // [32p + 8q4, 32p + 8q4 + 8) of step p.
@@ -292,19 +292,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // ---- this wave's blocks: jb = ks0 + 32*wave + 128*t; two register sets,
-  //      the next block's loads are in flight while one block computes ----
-  constexpr int kStride = 32 * kWaves;
+  // ---- this split's key blocks are split, split + S, split + 2S, ... and
+  //      wave w takes every 4th of them, so the S workgroups of a (sequence,
+  //      kv head) sweep the cache together, block by block: at any moment
+  //      the running workgroups read a few dense address ranges (friendly to
+  //      the DRAM pages), and near and far keys are spread evenly over the
+  //      splits.  Two register sets: the next block's loads are in flight
+  //      while one block computes. ----
+  const int kStride = 32 * a.S * kWaves;
   Regs RA, RB;
-  int jb = ks0 + 32 * wave;
-  if (jb < ks1) load_block(RA, jb);
-  while (jb < ks1) {
+  int jb = 32 * (split + a.S * wave);
+  if (jb < L) load_block(RA, jb);
+  while (jb < L) {
     const int jn = jb + kStride;
-    if (jn < ks1) load_block(RB, jn);
+    if (jn < L) load_block(RB, jn);
     compute_block(RA, jb);
-    if (jn >= ks1) break;
+    if (jn >= L) break;
     const int jn2 = jn + kStride;
-    if (jn2 < ks1) load_block(RA, jn2);
+    if (jn2 < L) load_block(RA, jn2);
     compute_block(RB, jn);
     jb = jn2;
   }

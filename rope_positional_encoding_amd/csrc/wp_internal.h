@@ -75,8 +75,7 @@ struct DecodeArgs {
   int64_t os_b, os_h;
   int B, Lmax, Hq, Hkv;
   int r;          // Hq / Hkv (<= 16)
-  int S;          // splits
-  int split_len;  // keys per split, multiple of kDecodeBN
+  int S;          // splits; split s takes key blocks s, s + S, s + 2S, ...
   float scale_log2;
   int cut[kMaxGroups];
 };
