@@ -67,6 +67,41 @@ def group_cutoffs(theta: float, d_h: int, G: int, pos_scale: float = 1.0) -> np.
     return per_dim.reshape(d_h // G, G).max(axis=1)
 
 
+def cutoffs_from_freqs(freqs, alpha: float = 2.0, trunc_channels=None) -> np.ndarray:
+    """Per-channel cutoffs from an arbitrary per-channel frequency vector
+    (radians per token, as the model rotates: any per-channel scaling
+    already applied).  The window is w_c = alpha * pi / f_c: alpha = 2 is one
+    period and alpha -> infinity prunes nothing; the kept integer distances
+    are those <= floor(w_c) ([notes] §2.1, the paragraph after Eq. (6) on
+    the pruning-strength knob alpha; §1.1 for cutoffs taken from the scaled
+    frequencies).  Only channels c < trunc_channels are truncated ("only the
+    first high-frequency channels", [notes] Appendix E summary and the
+    Fig. 8a ablation axes); the rest are never pruned.  Values clamp to
+    INT32_MAX."""
+    f = np.asarray(freqs, dtype=np.float64)
+    n_ch = f.shape[0]
+    if trunc_channels is None:
+        trunc_channels = n_ch
+    out = np.full(n_ch, INT32_MAX, dtype=np.int64)
+    if np.isinf(alpha):
+        return out
+    for c in range(min(trunc_channels, n_ch)):
+        w = alpha * np.pi / f[c]
+        out[c] = int(min(np.floor(w), float(INT32_MAX)))
+    return out
+
+
+def group_max(channel_cut: np.ndarray, G: int) -> np.ndarray:
+    """Group table from per-channel cutoffs: every dim inherits its channel's
+    cutoff and a group of G consecutive dims takes the largest
+    ([notes] §2.3, Eq. (8))."""
+    per_dim = np.repeat(np.asarray(channel_cut, dtype=np.int64), 2)
+    d_h = per_dim.shape[0]
+    if G % 2 or d_h % G:
+        raise ValueError("G must be even and divide d_h")
+    return per_dim.reshape(d_h // G, G).max(axis=1)
+
+
 def dim_cutoffs_exact(theta: float, d_h: int, pos_scale: float = 1.0) -> np.ndarray:
     """Per-dim cutoff of the exact per-channel rule (Eq. 6)."""
     return np.repeat(channel_cutoffs(theta, d_h, pos_scale), 2)

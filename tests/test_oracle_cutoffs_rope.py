@@ -84,6 +84,53 @@ def test_group_rule_structure():
             assert np.array_equal(g, ex.reshape(-1, G)[:, -1])   # = last dim of group
 
 
+def test_general_cutoffs_hand_computed():
+    # w_c = alpha * pi / f_c, kept distances <= floor(w_c); by hand:
+    # f = [1, 0.5, 0.25]: alpha 2 -> floor(2pi)=6, floor(4pi)=12, floor(8pi)=25
+    f = [1.0, 0.5, 0.25]
+    assert list(O.cutoffs_from_freqs(f, 2.0)) == [6, 12, 25]
+    # alpha 1 (half a period): floor(pi)=3, floor(2pi)=6, floor(4pi)=12
+    assert list(O.cutoffs_from_freqs(f, 1.0)) == [3, 6, 12]
+    # alpha 3: floor(3pi)=9, floor(6pi)=18, floor(12pi)=37
+    assert list(O.cutoffs_from_freqs(f, 3.0)) == [9, 18, 37]
+    # only the first channel truncated; the others never pruned
+    assert list(O.cutoffs_from_freqs(f, 2.0, trunc_channels=1)) == [6, O.INT32_MAX, O.INT32_MAX]
+    # nothing truncated, and alpha -> infinity, both prune nothing
+    assert all(v == O.INT32_MAX for v in O.cutoffs_from_freqs(f, 2.0, trunc_channels=0))
+    assert all(v == O.INT32_MAX for v in O.cutoffs_from_freqs(f, math.inf))
+    # a vanishing frequency clamps to the never-prune value
+    assert O.cutoffs_from_freqs([1e-12], 2.0)[0] == O.INT32_MAX
+    # group of two channels (G = 4) takes the larger: [6, 12] -> 12, [25] alone with G=2
+    assert list(O.group_max([6, 12], 4)) == [12]
+    assert list(O.group_max([6, 12, 25], 2)) == [6, 12, 25]
+
+
+def test_general_cutoffs_reduce_to_theta_schedule():
+    # with the plain schedule, alpha = 2 and every channel truncated, the
+    # general table is the theta table (itself pinned to Table 12 above)
+    for theta, d_h, s in [(1e4, 64, 1.0), (1e6, 128, 1.0), (1e6, 128, 4.0), (5e5, 128, 2.5)]:
+        f = O.frequencies(theta, d_h, s)
+        ch = O.cutoffs_from_freqs(f, 2.0)
+        assert np.array_equal(ch, O.channel_cutoffs(theta, d_h, s))
+        for G in (2, 16, 32):
+            assert np.array_equal(O.group_max(ch, G), O.group_cutoffs(theta, d_h, G, s))
+
+
+def test_general_cutoffs_monotone_in_alpha_and_truncation():
+    f = O.frequencies(1e6, 128)
+    prev = None
+    for alpha in (0.5, 1.0, 1.9, 2.0, 2.5, 8.0):
+        cur = O.cutoffs_from_freqs(f, alpha)
+        if prev is not None:
+            assert np.all(cur >= prev)
+        prev = cur
+    full = O.cutoffs_from_freqs(f, 2.0)
+    for k in (0, 1, 17, 63, 64):
+        part = O.cutoffs_from_freqs(f, 2.0, trunc_channels=k)
+        assert np.array_equal(part[:k], full[:k])
+        assert np.all(part[k:] == O.INT32_MAX)
+
+
 def test_rope_hand_example():
     # d_h = 4, theta = 100: f = (1, 0.1); position 3; x = (1, 0, 0, 1)
     x = np.array([[[1.0, 0.0, 0.0, 1.0]]])
