@@ -79,6 +79,32 @@ wp_status wp_group_cutoffs(double theta, int32_t d_h, int32_t G, double pos_scal
                            int32_t* out, int32_t out_len);
 
 /*
+ * wp_cutoffs_from_freqs -- the group cutoff table from any per-channel
+ * frequency vector (host only).
+ *
+ * freqs: host double[n_ch], n_ch = d_h / 2, the angular frequency of each
+ * channel in radians per position exactly as the model rotates (any
+ * per-channel or position scaling already applied: the cutoffs follow the
+ * scaled frequencies, [notes] section 1.1).  Channel c < trunc_channels keeps
+ * integer distances <= floor(alpha * pi / freqs[c]); channels from
+ * trunc_channels on are never pruned ([notes] section 2.1, the paragraph
+ * after Eq. (6): alpha = 2 is one period and alpha -> infinity prunes
+ * nothing; truncating only the first high-frequency channels is one of the
+ * ablations summarised around Fig. 8a and Appendix E).  A group of G dims
+ * takes the largest cutoff of its channels (section 2.3, Eq. (8)); values
+ * at or above 2^31-1 clamp to WP_NEVER_PRUNE.
+ * alpha > 0 (+infinity allowed); every freqs[c] finite and > 0;
+ * 0 <= trunc_channels <= n_ch; G even and dividing 2*n_ch;
+ * out: host int32[out_len], out_len == 2*n_ch / G.
+ * wp_prefill and wp_decode need a non-decreasing table: if the group
+ * cutoffs would decrease, the call returns WP_ERR_ARG and leaves out
+ * untouched.  With freqs[c] = theta^(-2c/d_h) / pos_scale, alpha = 2 and
+ * trunc_channels = n_ch the result equals wp_group_cutoffs.
+ */
+wp_status wp_cutoffs_from_freqs(const double* freqs, int32_t n_ch, double alpha, int32_t trunc_channels,
+                                int32_t G, int32_t* out, int32_t out_len);
+
+/*
  * wp_rope_apply -- rotate every channel of x by its position's angle.
  *
  * x: [B, n, H, d_h], dtype WP_DTYPE_BF16 or WP_DTYPE_F32, strides

@@ -41,6 +41,7 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 
 _SIGNATURES = {
     "wp_group_cutoffs": (_i32, [_dbl, _i32, _i32, _dbl, _I32P, _i32]),
+    "wp_cutoffs_from_freqs": (_i32, [ctypes.POINTER(ctypes.c_double), _i32, _dbl, _i32, _i32, _I32P, _i32]),
     "wp_rope_apply": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _I64P, _I64P, _vp, _dbl, _dbl, _vp]),
     "wp_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P, _i32,
                           _u32, _vp, _vp]),
@@ -127,6 +128,23 @@ def group_cutoffs(theta: float, d_h: int, G: int, pos_scale: float = 1.0) -> lis
     ng = d_h // G
     out = (ctypes.c_int32 * max(ng, 1))()
     _check(lib().wp_group_cutoffs(float(theta), int(d_h), int(G), float(pos_scale), out, ng))
+    return [int(v) for v in out[:ng]]
+
+
+def cutoffs_from_freqs(freqs: Sequence[float], G: int, alpha: float = 2.0,
+                       trunc_channels: Optional[int] = None) -> list:
+    """Group cutoff table from a per-channel frequency vector (radians per
+    position, scaling applied), the window alpha*pi/f and the number of
+    leading channels that are truncated (default: all)."""
+    n_ch = len(freqs)
+    if trunc_channels is None:
+        trunc_channels = n_ch
+    if G <= 0 or (2 * n_ch) % G:
+        raise ValueError("G must divide 2 * len(freqs)")
+    ng = 2 * n_ch // G
+    f = (ctypes.c_double * max(n_ch, 1))(*[float(x) for x in freqs])
+    out = (ctypes.c_int32 * max(ng, 1))()
+    _check(lib().wp_cutoffs_from_freqs(f, n_ch, float(alpha), int(trunc_channels), int(G), out, ng))
     return [int(v) for v in out[:ng]]
 
 

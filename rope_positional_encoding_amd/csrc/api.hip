@@ -8,6 +8,8 @@
 #include "../../include/waveprune.h"
 #include "wp_internal.h"
 
+#include <vector>
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -106,6 +108,41 @@ wp_status wp_group_cutoffs(double theta, int32_t d_h, int32_t G, double pos_scal
     }
     out[g] = (best >= 2147483647.0 || !isfinite(best)) ? WP_NEVER_PRUNE : (int32_t)best;
   }
+  return ok();
+}
+
+wp_status wp_cutoffs_from_freqs(const double* freqs, int32_t n_ch, double alpha, int32_t trunc_channels,
+                                int32_t G, int32_t* out, int32_t out_len) {
+  if (!freqs || !out) return fail(WP_ERR_NULL, "freqs/out is NULL");
+  if (n_ch <= 0) return fail(WP_ERR_SHAPE, "n_ch = %d must be positive", n_ch);
+  if (trunc_channels < 0 || trunc_channels > n_ch)
+    return fail(WP_ERR_SHAPE, "trunc_channels = %d must be in [0, n_ch = %d]", trunc_channels, n_ch);
+  if (G <= 0 || G % 2 || (2 * (int64_t)n_ch) % G)
+    return fail(WP_ERR_SHAPE, "G = %d must be even and divide d_h = 2*n_ch = %lld", G, 2LL * n_ch);
+  if ((int64_t)out_len * G != 2 * (int64_t)n_ch)
+    return fail(WP_ERR_SHAPE, "out_len = %d, expected 2*n_ch/G = %lld", out_len, 2LL * n_ch / G);
+  if (!(alpha > 0.0)) return fail(WP_ERR_ARG, "alpha must be > 0 (or +infinity)");
+  for (int c = 0; c < n_ch; ++c)
+    if (!(freqs[c] > 0.0) || !isfinite(freqs[c]))
+      return fail(WP_ERR_ARG, "freqs[%d] must be finite and > 0", c);
+  const double pi = 3.14159265358979323846264338327950288;
+  std::vector<int32_t> tab(out_len);
+  for (int g = 0; g < out_len; ++g) {
+    double best = -1.0;
+    // channels of dims [gG, (g+1)G) are c = gG/2 .. (g+1)G/2 - 1
+    for (int c = g * G / 2; c < (g + 1) * G / 2; ++c) {
+      // window alpha*pi/f_c; channels from trunc_channels on are never pruned
+      const double w = (c < trunc_channels && isfinite(alpha)) ? floor(alpha * pi / freqs[c]) : INFINITY;
+      if (w > best) best = w;
+    }
+    tab[g] = (best >= 2147483647.0 || !isfinite(best)) ? WP_NEVER_PRUNE : (int32_t)best;
+  }
+  for (int g = 1; g < out_len; ++g)
+    if (tab[g] < tab[g - 1])
+      return fail(WP_ERR_ARG, "group cutoffs decrease at group %d (%d < %d): the kernels need a "
+                              "non-decreasing table (frequencies non-increasing over the groups)",
+                  g, tab[g], tab[g - 1]);
+  for (int g = 0; g < out_len; ++g) out[g] = tab[g];
   return ok();
 }
 

@@ -3,6 +3,7 @@ header declares; host-only calls (cutoff table, tiling, host tile classifier)
 agree bit-exactly with the oracle; invalid arguments are rejected before any
 HIP call (so these run without a GPU)."""
 import ctypes
+import math
 import os
 import re
 
@@ -48,6 +49,67 @@ def test_group_cutoffs_clamp_never_prune():
     got = W.group_cutoffs(1e12, 128, 16, 1e6)
     assert got[-1] == W.NEVER_PRUNE
     assert got == [int(v) for v in O.group_cutoffs(1e12, 128, 16, 1e6)]
+
+
+def _ramp_scaled_freqs(theta, d_h, s, lo=0.25, hi=0.75):
+    """A per-channel scaled schedule: the first `lo` fraction of channels
+    keep their frequency, the last (1 - hi) are divided by s, and the ones in
+    between are divided by a factor that ramps linearly from 1 to s."""
+    n = d_h // 2
+    f = O.frequencies(theta, d_h)
+    out = []
+    for c in range(n):
+        t = min(1.0, max(0.0, (c / (n - 1) - lo) / (hi - lo)))
+        out.append(f[c] / (1.0 + t * (s - 1.0)))
+    return out
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 1.7, 2.0, 2.5, 4.0, math.inf])
+@pytest.mark.parametrize("trunc", [None, 0, 1, 8, 40])
+def test_general_cutoffs_match_oracle(alpha, trunc):
+    cases = [list(O.frequencies(1e6, 128)), list(O.frequencies(1e4, 64, 4.0)),
+             _ramp_scaled_freqs(1e6, 128, 8.0), _ramp_scaled_freqs(5e5, 64, 32.0)]
+    for f in cases:
+        n_ch = len(f)
+        k = n_ch if trunc is None else min(trunc, n_ch)
+        ch = O.cutoffs_from_freqs(f, alpha, k)
+        for G in (2, 4, 16, 32):
+            if (2 * n_ch) % G:
+                continue
+            got = W.cutoffs_from_freqs(f, G, alpha, k)
+            assert got == [int(v) for v in O.group_max(ch, G)], (alpha, k, G)
+
+
+def test_general_cutoffs_equal_theta_table():
+    for theta, d_h, s in [(1e4, 64, 1.0), (1e6, 128, 1.0), (1e6, 128, 4.0)]:
+        f = list(O.frequencies(theta, d_h, s))
+        for G in (16, 32):
+            assert W.cutoffs_from_freqs(f, G) == W.group_cutoffs(theta, d_h, G, s)
+
+
+def test_general_cutoffs_validation():
+    f = list(O.frequencies(1e6, 128))
+    L = W.lib()
+    out = (ctypes.c_int32 * 8)()
+    arr = (ctypes.c_double * 64)(*f)
+    assert L.wp_cutoffs_from_freqs(None, 64, 2.0, 64, 16, out, 8) == -1
+    assert L.wp_cutoffs_from_freqs(arr, 64, 2.0, 64, 16, None, 8) == -1
+    assert L.wp_cutoffs_from_freqs(arr, 0, 2.0, 0, 16, out, 0) == -2
+    assert L.wp_cutoffs_from_freqs(arr, 64, 2.0, 65, 16, out, 8) == -2      # trunc > n_ch
+    assert L.wp_cutoffs_from_freqs(arr, 64, 2.0, -1, 16, out, 8) == -2
+    assert L.wp_cutoffs_from_freqs(arr, 64, 2.0, 64, 12, out, 8) == -2      # G does not divide 128
+    assert L.wp_cutoffs_from_freqs(arr, 64, 2.0, 64, 16, out, 7) == -2      # out_len
+    assert L.wp_cutoffs_from_freqs(arr, 64, 0.0, 64, 16, out, 8) == -6      # alpha
+    assert L.wp_cutoffs_from_freqs(arr, 64, math.nan, 64, 16, out, 8) == -6
+    bad = (ctypes.c_double * 64)(*([0.0] + f[1:]))
+    assert L.wp_cutoffs_from_freqs(bad, 64, 2.0, 64, 16, out, 8) == -6      # zero frequency
+    # increasing frequencies give a decreasing table: rejected, out untouched
+    rev = (ctypes.c_double * 64)(*reversed(f))
+    for i in range(8):
+        out[i] = -7
+    assert L.wp_cutoffs_from_freqs(rev, 64, 2.0, 64, 16, out, 8) == -6
+    assert list(out) == [-7] * 8
+    assert b"non-decreasing" in L.wp_last_error()
 
 
 def test_tiling_queries():
