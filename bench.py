@@ -159,6 +159,38 @@ def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512
     }
 
 
+def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
+    """The same decode with K read from the group-major compact store (group
+    g keeps only its last D'_g + 1 keys): 10 warmups, median of 50."""
+    import torch
+    log("bench: decode from the compact K store")
+    B, L, Hkv, d = kc.shape
+    store = W.kcache_empty(B, Hkv, L, d, G, cut, device=kc.device)
+    W.kcache_append(kc, torch.zeros(B, dtype=torch.int32, device=kc.device), store, L, cut, G)
+    for _ in range(10):
+        W.decode_kcache(q, store, vc, cl, qp, cut, G, workspace=ws, out=od)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        W.decode_kcache(q, store, vc, cl, qp, cut, G, workspace=ws, out=od)
+        e1.record(s)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ts]
+    med = statistics.median(ms)
+    k_full = float(kc.numel() * 2)
+    k_store = float(store.numel() * 2)
+    return {"ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+            "algorithmic_gbs": round(dec_alg / (med * 1e-3) / 1e9, 1),
+            "k_store_bytes": k_store, "k_cache_bytes": k_full,
+            "k_capacity_fraction": round(k_store / k_full, 4),
+            "kv_capacity_fraction": round((k_store + k_full) / (2 * k_full), 4),
+            "time_vs_full_cache_decode": round(med / full_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +199,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-kcache", action="store_true", help="skip the compact K store decode line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches): a kernel of known "
                          "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -320,6 +353,9 @@ def main():
                               "traffic": measured_traffic("decode"), "algorithmic_bytes": dec_alg,
                               "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
                               "avg_ms": round(avg["decode"], 4)}
+    if not args.no_kcache:
+        out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kc, vc, cl, qp, cut, G, ws, od, dec_alg,
+                                            med["decode"])
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)

@@ -191,6 +191,66 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     uint32_t flags, int64_t* counters, void* stream);
 
+/*
+ * Group-major compact K cache.
+ *
+ * Group g of a key is only read while the query is within D'_g of it, and a
+ * decoding query never moves back, so group g needs only the keys of the
+ * last D'_g + 1 positions.  Keeping just those turns decode's skipped K
+ * reads into allocated-capacity savings: the pages leave per-channel
+ * eviction of expired K entries as future work and note that fewer reads
+ * and a smaller allocated cache are separate gains ([notes] section 2.3,
+ * the closing paragraph on what the implementation optimises).
+ *
+ * The store of one (sequence, kv head) is ng = d_h/G rings, one per group,
+ * concatenated: group g has cap[g] = min(Lmax, cutoffs[g] + 1) slots of G
+ * bf16 elements at element offset off[g] (off[0] = 0, off[g+1] = off[g] +
+ * cap[g]*G); key j of group g sits in slot j % cap[g], so the keys of a
+ * group are contiguous and a decode step reads each kept group as one dense
+ * run.  A store is addressed with two strides, sequence and kv head, in
+ * elements.  The cutoffs passed to every call on one store must be the same
+ * table.
+ */
+
+/* wp_kcache_layout -- ring sizes caps[ng] and element offsets offsets[ng+1]
+ * (offsets[ng] = elements per (sequence, kv head)) of the compact K store
+ * (host only).  cutoffs: host int32[d_h/G], non-decreasing, >= 0. */
+wp_status wp_kcache_layout(int32_t Lmax, int32_t d_h, int32_t G, const int32_t* cutoffs, int32_t* caps,
+                           int64_t* offsets);
+
+/*
+ * wp_kcache_append -- write T rotated keys per sequence into the compact
+ * store.  k [B, T, Hkv, d_h] bf16, k_strides = {batch, token, head}; token
+ * t of sequence b is position pos0[b] + t (pos0: device int32[B], >= 0;
+ * the caller keeps pos0[b] + T <= Lmax).  For each group, a key that a
+ * later token of the same call replaces in its ring is not written, so the
+ * result is the ring after appending the tokens in order.  Appends must be
+ * in position order across calls (prefill once, then one token per step).
+ * store_strides = {sequence, kv head} >= offsets[ng] elements, regions not
+ * overlapping.  Asynchronous on stream.
+ */
+wp_status wp_kcache_append(const void* k, int32_t B, int32_t T, int32_t Hkv, int32_t d_h,
+                           const int64_t k_strides[3], const int32_t* pos0, void* store,
+                           const int64_t store_strides[2], int32_t Lmax, const int32_t* cutoffs, int32_t G,
+                           void* stream);
+
+/*
+ * wp_decode_kcache -- wp_decode with K read from the compact store.
+ * strides[9] = {q_b, q_h, store_b, store_h, v_b, v_t, v_h, o_b, o_h}.  The
+ * store must hold the keys of positions 0 .. cache_len[b]-1 (appended in
+ * order); V is the ordinary cache [B, Lmax, Hkv, d_h].  Keys are read only
+ * for groups a key block keeps; a partial group's keys beyond its cutoff may
+ * find their slot reused and are masked, as in wp_decode.  Same results as
+ * wp_decode on the full cache (the same arithmetic in the same order).
+ * WP_FLAG_DENSE is rejected (WP_ERR_ARG); cutoffs must not be NULL;
+ * Lmax <= 2^24.  Workspace as for wp_decode.
+ */
+wp_status wp_decode_kcache(const void* q, const void* k_store, const void* v_cache, void* o,
+                           const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
+                           int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[9],
+                           const int32_t* cutoffs, int32_t G, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, int64_t* counters, void* stream);
+
 /* Number of key splits wp_decode uses when num_splits == 0: the count that
  * spreads B * Hkv * splits workgroups over the current device's compute
  * units with the fewest keys per unit (at least 128 keys per split). */

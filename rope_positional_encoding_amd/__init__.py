@@ -47,6 +47,10 @@ _SIGNATURES = {
                           _u32, _vp, _vp]),
     "wp_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P, _i32,
                          _i32, _vp, _sz, _u32, _vp, _vp]),
+    "wp_kcache_layout": (_i32, [_i32, _i32, _i32, _I32P, _I32P, _I64P]),
+    "wp_kcache_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _I64P, _vp, _vp, _I64P, _i32, _I32P, _i32, _vp]),
+    "wp_decode_kcache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P,
+                                _i32, _i32, _vp, _sz, _u32, _vp, _vp]),
     "wp_decode_num_splits": (_i32, [_i32, _i32, _i32]),
     "wp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "wp_prefill_tiling": (_i32, [_i32, _i32, _I32P, _I32P]),
@@ -262,5 +266,71 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check(lib().wp_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_len), _ptr(q_pos), B, Lmax, Hq,
         Hkv, d, _i64arr(strides), cut, int(G), int(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), flags, _ptr(counters), _stream(q)))
+    return out
+
+
+def kcache_layout(Lmax: int, d_h: int, G: int, cutoffs: Sequence[int]):
+    """Ring sizes (caps[ng]) and element offsets (offsets[ng+1]) of the
+    group-major compact K store of one (sequence, kv head)."""
+    ng = d_h // G
+    caps = (ctypes.c_int32 * max(ng, 1))()
+    offs = (ctypes.c_int64 * (ng + 1))()
+    _check(lib().wp_kcache_layout(int(Lmax), int(d_h), int(G), _i32arr(cutoffs), caps, offs))
+    return [int(v) for v in caps[:ng]], [int(v) for v in offs]
+
+
+def kcache_empty(B: int, Hkv: int, Lmax: int, d_h: int, G: int, cutoffs: Sequence[int],
+                 device=None) -> torch.Tensor:
+    """An uninitialised compact K store [B, Hkv, elements] (bf16)."""
+    _, offs = kcache_layout(Lmax, d_h, G, cutoffs)
+    return torch.empty((B, Hkv, offs[-1]), dtype=torch.bfloat16, device=device)
+
+
+def kcache_append(k: torch.Tensor, pos0: torch.Tensor, store: torch.Tensor, Lmax: int,
+                  cutoffs: Sequence[int], G: int) -> torch.Tensor:
+    """Write k [B, T, Hkv, d_h] (rotated bf16) at positions pos0[b] + t
+    (device int32 [B]) into the compact store [B, Hkv, elements]."""
+    _need(k, "k", torch.bfloat16, 4)
+    _need(pos0, "pos0", torch.int32, 1)
+    _need(store, "store", torch.bfloat16, 3)
+    B, T, Hkv, d = k.shape
+    if store.shape[0] != B or store.shape[1] != Hkv or store.stride(2) != 1:
+        raise ValueError("store must be [B, Hkv, elements] (elements contiguous) matching k")
+    _check(lib().wp_kcache_append(
+        _ptr(k), B, T, Hkv, d, _i64arr(list(k.stride()[:3])), _ptr(pos0), _ptr(store),
+        _i64arr(list(store.stride()[:2])), int(Lmax), _i32arr(cutoffs), int(G), _stream(k)))
+    return store
+
+
+def decode_kcache(q: torch.Tensor, store: torch.Tensor, v_cache: torch.Tensor,
+                  cache_len: torch.Tensor, q_pos: torch.Tensor, cutoffs: Sequence[int], G: int,
+                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                  counters: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """wp_decode with K from the compact store [B, Hkv, elements]; v_cache
+    [B, Lmax, Hkv, d_h]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(store, "store", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    B, Hq, d = q.shape
+    Lmax, Hkv = v_cache.shape[1], v_cache.shape[2]
+    if (tuple(v_cache.shape) != (B, Lmax, Hkv, d) or store.shape[0] != B or store.shape[1] != Hkv
+            or store.stride(2) != 1):
+        raise ValueError("v_cache must be [B, Lmax, Hkv, d_h] and store [B, Hkv, elements]")
+    need = decode_workspace_size(B, Lmax, Hq, Hkv, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    flags = FLAG_COUNT if counters is not None else 0
+    strides = (list(q.stride()[:2]) + list(store.stride()[:2]) + list(v_cache.stride()[:3])
+               + list(out.stride()[:2]))
+    _check(lib().wp_decode_kcache(
+        _ptr(q), _ptr(store), _ptr(v_cache), _ptr(out), _ptr(cache_len), _ptr(q_pos), B, Lmax, Hq,
+        Hkv, d, _i64arr(strides), _i32arr(cutoffs), int(G), int(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), flags, _ptr(counters), _stream(q)))
     return out

@@ -349,16 +349,30 @@ size_t wp_decode_workspace_size(int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv
   return align256(rows * d_h * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
-wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
-                    const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
-                    int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[10],
-                    const int32_t* cutoffs, int32_t G, int32_t num_splits, void* workspace,
-                    size_t workspace_bytes, uint32_t flags, int64_t* counters, void* stream) {
-  if (!q || !k_cache || !v_cache || !o || !cache_len || !q_pos || !strides || !workspace)
-    return fail(WP_ERR_NULL, "a required pointer is NULL");
+namespace {
+// ring sizes and element offsets of the compact K store of one (sequence,
+// kv head): group g keeps the last min(Lmax, cutoffs[g] + 1) keys
+void kcache_geometry(int32_t Lmax, int32_t ng, int32_t G, const int32_t* cut, int* cap, int64_t* off) {
+  off[0] = 0;
+  for (int g = 0; g < ng; ++g) {
+    const int64_t c = (int64_t)cut[g] + 1;
+    cap[g] = (int)(c < Lmax ? c : Lmax);
+    off[g + 1] = off[g] + (int64_t)cap[g] * G;
+  }
+}
+
+// shared by wp_decode and wp_decode_kcache; st10 = {q_b, q_h, k_b, k_t, k_h,
+// v_b, v_t, v_h, o_b, o_h} (for the compact store k_b, k_h are its sequence
+// and kv-head strides and k_t is unused)
+wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o, const int32_t* cache_len,
+                      const int32_t* q_pos, int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv, int32_t d_h,
+                      const int64_t st10[10], const int32_t* cutoffs, int32_t G, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, uint32_t flags, int64_t* counters,
+                      void* stream, bool compact) {
   if (flags & ~(WP_FLAG_DENSE | WP_FLAG_COUNT)) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
   const bool dense = flags & WP_FLAG_DENSE;
   const bool count = flags & WP_FLAG_COUNT;
+  if (compact && dense) return fail(WP_ERR_ARG, "WP_FLAG_DENSE does not apply to the compact K store");
   if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
   if (count && !counters) return fail(WP_ERR_NULL, "counters is NULL with WP_FLAG_COUNT");
   if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
@@ -366,19 +380,19 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(WP_ERR_UNSUPPORTED, "decode supports at most 16 query heads per kv head");
   if (num_splits < 0) return fail(WP_ERR_ARG, "num_splits must be >= 0");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(WP_ERR_ALIGN, "q, k_cache, v_cache, o must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v_cache) || !aligned16(o))
+    return fail(WP_ERR_ALIGN, "q, the K cache or store, v_cache, o must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(WP_ERR_ALIGN, "workspace must be 256-byte aligned");
   if ((reinterpret_cast<uintptr_t>(cache_len) & 3u) || (reinterpret_cast<uintptr_t>(q_pos) & 3u))
     return fail(WP_ERR_ALIGN, "cache_len / q_pos misaligned");
   if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
     return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
-  if (wp_status s = check_strides(strides, 10)) return s;
-  if (strides[3] < d_h || strides[6] < d_h)
+  if (wp_status s = check_strides(st10, 10)) return s;
+  if ((!compact && st10[3] < d_h) || st10[6] < d_h)
     return fail(WP_ERR_SHAPE, "k/v cache token strides must be >= d_h");
-  if ((int64_t)(Lmax - 1) * strides[3] * 2 + 2 * d_h >= 2147483647LL ||
-      (int64_t)(Lmax - 1) * strides[6] * 2 + 2 * d_h >= 2147483647LL)
+  if ((!compact && (int64_t)(Lmax - 1) * st10[3] * 2 + 2 * d_h >= 2147483647LL) ||
+      (int64_t)(Lmax - 1) * st10[6] * 2 + 2 * d_h >= 2147483647LL)
     return fail(WP_ERR_SHAPE, "one sequence of the K or V cache spans 2^31 bytes or more");
   const size_t need = wp_decode_workspace_size(B, Lmax, Hq, Hkv, d_h, num_splits);
   if (workspace_bytes < need)
@@ -392,10 +406,21 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
     if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
     for (int g = 0; g < ng; ++g) a.cut[g] = cutoffs[g];
   }
+  if (compact) {
+    if (Lmax > (1 << 24)) return fail(WP_ERR_SHAPE, "the compact K store supports Lmax <= 2^24");
+    int64_t off[wp::kMaxGroups + 1];
+    kcache_geometry(Lmax, ng, G, cutoffs, a.kcap, off);
+    if (st10[2] < off[ng] || st10[4] < off[ng])
+      return fail(WP_ERR_SHAPE, "K store strides must be >= the store size (%lld elements)", (long long)off[ng]);
+    if (off[ng] * 2 >= 2147483647LL) return fail(WP_ERR_SHAPE, "one K store spans 2^31 bytes or more");
+    for (int g = 0; g < ng; ++g) a.koff[g] = (int)off[g];
+    a.kstore_elems = (int)off[ng];
+    a.compact = 1;
+  }
   const int S = decode_splits(B, Lmax, Hkv, num_splits);
   const size_t rows = (size_t)B * Hq * S;
   a.q = static_cast<const wp::bf16*>(q);
-  a.k = static_cast<const wp::bf16*>(k_cache);
+  a.k = static_cast<const wp::bf16*>(k);
   a.v = static_cast<const wp::bf16*>(v_cache);
   a.o = static_cast<wp::bf16*>(o);
   a.cache_len = cache_len;
@@ -403,10 +428,10 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * d_h * sizeof(float)));
   a.counters = reinterpret_cast<unsigned long long*>(counters);
-  a.qs_b = strides[0]; a.qs_h = strides[1];
-  a.ks_b = strides[2]; a.ks_t = strides[3]; a.ks_h = strides[4];
-  a.vs_b = strides[5]; a.vs_t = strides[6]; a.vs_h = strides[7];
-  a.os_b = strides[8]; a.os_h = strides[9];
+  a.qs_b = st10[0]; a.qs_h = st10[1];
+  a.ks_b = st10[2]; a.ks_t = st10[3]; a.ks_h = st10[4];
+  a.vs_b = st10[5]; a.vs_t = st10[6]; a.vs_h = st10[7];
+  a.os_b = st10[8]; a.os_h = st10[9];
   a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv;
   a.r = Hq / Hkv;
   a.S = S;
@@ -417,6 +442,82 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
   hipError_t e = wp::launch_decode(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                    const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
+                    int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[10],
+                    const int32_t* cutoffs, int32_t G, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, uint32_t flags, int64_t* counters, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !cache_len || !q_pos || !strides || !workspace)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  return decode_impl(q, k_cache, v_cache, o, cache_len, q_pos, B, Lmax, Hq, Hkv, d_h, strides, cutoffs, G,
+                     num_splits, workspace, workspace_bytes, flags, counters, stream, false);
+}
+
+wp_status wp_kcache_layout(int32_t Lmax, int32_t d_h, int32_t G, const int32_t* cutoffs, int32_t* caps,
+                           int64_t* offsets) {
+  if (!cutoffs || !caps || !offsets) return fail(WP_ERR_NULL, "cutoffs/caps/offsets is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (Lmax < 1) return fail(WP_ERR_SHAPE, "Lmax must be >= 1");
+  const int ng = d_h / G;
+  if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+  int cap[wp::kMaxGroups];
+  int64_t off[wp::kMaxGroups + 1];
+  kcache_geometry(Lmax, ng, G, cutoffs, cap, off);
+  for (int g = 0; g < ng; ++g) caps[g] = cap[g];
+  for (int g = 0; g <= ng; ++g) offsets[g] = off[g];
+  return ok();
+}
+
+wp_status wp_kcache_append(const void* k, int32_t B, int32_t T, int32_t Hkv, int32_t d_h,
+                           const int64_t k_strides[3], const int32_t* pos0, void* store,
+                           const int64_t store_strides[2], int32_t Lmax, const int32_t* cutoffs, int32_t G,
+                           void* stream) {
+  if (!k || !k_strides || !pos0 || !store || !store_strides || !cutoffs)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (B < 1 || T < 1 || Hkv < 1 || Lmax < 1) return fail(WP_ERR_SHAPE, "B, T, Hkv, Lmax must be >= 1");
+  if (T > Lmax) return fail(WP_ERR_SHAPE, "T = %d exceeds Lmax = %d", T, Lmax);
+  if (Lmax > (1 << 24)) return fail(WP_ERR_SHAPE, "the compact K store supports Lmax <= 2^24");
+  if (!aligned16(k) || !aligned16(store)) return fail(WP_ERR_ALIGN, "k and store must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(pos0) & 3u) return fail(WP_ERR_ALIGN, "pos0 misaligned");
+  if (wp_status s = check_strides(k_strides, 3)) return s;
+  if (wp_status s = check_strides(store_strides, 2)) return s;
+  const int ng = d_h / G;
+  if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+  wp::KAppendArgs a;
+  memset(&a, 0, sizeof(a));
+  int64_t off[wp::kMaxGroups + 1];
+  kcache_geometry(Lmax, ng, G, cutoffs, a.kcap, off);
+  if (store_strides[0] < off[ng] || store_strides[1] < off[ng])
+    return fail(WP_ERR_SHAPE, "store strides must be >= the store size (%lld elements)", (long long)off[ng]);
+  if (off[ng] * 2 >= 2147483647LL) return fail(WP_ERR_SHAPE, "one K store spans 2^31 bytes or more");
+  for (int g = 0; g < ng; ++g) a.koff[g] = (int)off[g];
+  a.k = static_cast<const wp::bf16*>(k);
+  a.store = static_cast<wp::bf16*>(store);
+  a.pos0 = pos0;
+  a.ks_b = k_strides[0]; a.ks_t = k_strides[1]; a.ks_h = k_strides[2];
+  a.ss_b = store_strides[0]; a.ss_h = store_strides[1];
+  a.B = B; a.T = T; a.Hkv = Hkv; a.d_h = d_h; a.G = G; a.ng = ng;
+  if ((long long)B * T * Hkv * (d_h / 8) / 256 + 1 > 2147483647LL) return fail(WP_ERR_SHAPE, "grid too large");
+  hipError_t e = wp::launch_kcache_append(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "kcache append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wp_status wp_decode_kcache(const void* q, const void* k_store, const void* v_cache, void* o,
+                           const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
+                           int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[9],
+                           const int32_t* cutoffs, int32_t G, int32_t num_splits, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, int64_t* counters, void* stream) {
+  if (!q || !k_store || !v_cache || !o || !cache_len || !q_pos || !strides || !workspace || !cutoffs)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  const int64_t st10[10] = {strides[0], strides[1], strides[2], 0, strides[3],
+                            strides[4], strides[5], strides[6], strides[7], strides[8]};
+  return decode_impl(q, k_store, v_cache, o, cache_len, q_pos, B, Lmax, Hq, Hkv, d_h, st10, cutoffs, G,
+                     num_splits, workspace, workspace_bytes, flags, counters, stream, true);
 }
 
 }  // extern "C"

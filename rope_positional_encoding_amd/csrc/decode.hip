@@ -65,7 +65,17 @@ __device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) 
 // are stored at positions [8q, 8q+8).
 __device__ inline int vt_pos32(int kq) { return kq < 4 ? 8 * kq : 8 * (kq - 4) + 4; }
 
-template <int D, int G, bool COUNT>
+// j mod c for 0 <= j < 2^24 and 1 <= c < 2^24, with rc = 1/c rounded to
+// float: the float quotient is off by at most one, which the two
+// corrections remove.
+__device__ inline int mod_small(int j, int c, float rc) {
+  int r = j - (int)((float)j * rc) * c;
+  r += (r < 0) ? c : 0;
+  r -= (r >= c) ? c : 0;
+  return r;
+}
+
+template <int D, int G, bool COUNT, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int NP = D / 32;          // 32-dim MFMA steps of QK
   constexpr int NG = D / G;           // groups
@@ -111,7 +121,25 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int krow_b = (int)(a.ks_t * 2);
   const int vrow_b = (int)(a.vs_t * 2);
   const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(
-      a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h, L > 0 ? (L - 1) * krow_b + 2 * D : 0);
+      a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h,
+      COMPACT ? 2 * a.kstore_elems : (L > 0 ? (L - 1) * krow_b + 2 * D : 0));
+  // compact store: ring size, its reciprocal and the ring's byte offset for
+  // the group this lane reads in QK step p.  The kernel arguments are read
+  // with uniform indices only (a lane-dependent index would turn them into
+  // per-lane memory loads, whose waits would also drain the K/V loads in
+  // flight).
+  int kcap_p[NP], kbase_p[NP];
+  float rcap_p[NP];
+  if (COMPACT) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int gl = (32 * p) / G, gh = (32 * p + 24) / G;
+      const bool lo = ((32 * p + 8 * q4) / G) == gl;
+      kcap_p[p] = lo ? a.kcap[gl] : a.kcap[gh];
+      kbase_p[p] = (lo ? a.koff[gl] : a.koff[gh]) * 2;
+      rcap_p[p] = 1.0f / (float)kcap_p[p];
+    }
+  }
   const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(
       a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h, L > 0 ? (L - 1) * vrow_b + 2 * D : 0);
   constexpr int kOut = 0x7ffffff0;    // any offset >= the resource size
@@ -158,11 +186,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     classify(jb, sL, sR);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int row = (jb + 16 * blk + n16) * krow_b;
+      const int j = jb + 16 * blk + n16;
+      const int row = j * krow_b;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int g = (32 * p + 8 * q4) / G;      // this lane's group in step p
-        const int off = (g >= sL) ? row + (32 * p + 8 * q4) * 2 : kOut;
+        const int dim = 32 * p + 8 * q4;
+        const int g = dim / G;                    // this lane's group in step p
+        int off;
+        if (COMPACT) {
+          const int slot = mod_small(j, kcap_p[p], rcap_p[p]);
+          off = (g >= sL && j < L) ? kbase_p[p] + (slot * G + dim % G) * 2 : kOut;
+        } else {
+          off = (g >= sL) ? row + dim * 2 : kOut;
+        }
         R.k[blk][p] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
       }
     }
@@ -396,28 +432,69 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int e = 0; e < PER; ++e) op[lane + 64 * e] = static_cast<__bf16>(acc[e] * inv);
 }
 
-template <int D, int G>
+template <int D, int G, bool COMPACT>
 hipError_t launch_dg(const DecodeArgs& a, bool count, hipStream_t s) {
   const long long blocks = (long long)a.B * a.Hkv * a.S;
   if (blocks <= 0) return hipSuccess;
   if (count)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, true, COMPACT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, false, COMPACT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
+template <int D, int G>
+hipError_t launch_dgc(const DecodeArgs& a, bool count, hipStream_t s) {
+  return a.compact ? launch_dg<D, G, true>(a, count, s) : launch_dg<D, G, false>(a, count, s);
+}
+
+// One thread per 16-byte chunk of a key row: the chunk's group g sends it
+// to slot (pos0[b] + t) % kcap[g] of that group's ring.  Tokens that a later
+// token of the same call would overwrite (t < T - kcap[g]) are skipped, so
+// the result does not depend on the order of the writes.
+__global__ __launch_bounds__(256) void kcache_append_kernel(KAppendArgs a) {
+  const int cpr = a.d_h / 8;                               // chunks per row
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)a.B * a.T * a.Hkv * cpr;
+  if (idx >= total) return;
+  const int c = (int)(idx % cpr);
+  long long r = idx / cpr;
+  const int h = (int)(r % a.Hkv);
+  r /= a.Hkv;
+  const int t = (int)(r % a.T);
+  const int b = (int)(r / a.T);
+  const int g = (8 * c) / a.G;
+  const int cap = a.kcap[g];
+  if (t < a.T - cap) return;
+  const long long pos = (long long)a.pos0[b] + t;
+  if (pos < 0) return;
+  const int slot = (int)(pos % cap);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(a.k + (int64_t)b * a.ks_b + (int64_t)t * a.ks_t +
+                                                   (int64_t)h * a.ks_h + 8 * c);
+  bf16* dst = a.store + (int64_t)b * a.ss_b + (int64_t)h * a.ss_h + a.koff[g] + (int64_t)slot * a.G +
+              (8 * c) % a.G;
+  *reinterpret_cast<u32x4*>(dst) = v;
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s) {
-  if (d_h == 128 && G == 16) return launch_dg<128, 16>(a, count, s);
-  if (d_h == 128 && G == 32) return launch_dg<128, 32>(a, count, s);
-  if (d_h == 64 && G == 16) return launch_dg<64, 16>(a, count, s);
-  if (d_h == 64 && G == 32) return launch_dg<64, 32>(a, count, s);
+  if (d_h == 128 && G == 16) return launch_dgc<128, 16>(a, count, s);
+  if (d_h == 128 && G == 32) return launch_dgc<128, 32>(a, count, s);
+  if (d_h == 64 && G == 16) return launch_dgc<64, 16>(a, count, s);
+  if (d_h == 64 && G == 32) return launch_dgc<64, 32>(a, count, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_kcache_append(const KAppendArgs& a, hipStream_t s) {
+  const long long total = (long long)a.B * a.T * a.Hkv * (a.d_h / 8);
+  if (total <= 0) return hipSuccess;
+  const long long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(kcache_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace wp

@@ -78,10 +78,34 @@ struct DecodeArgs {
   int S;          // splits; split s takes key blocks s, s + S, s + 2S, ...
   float scale_log2;
   int cut[kMaxGroups];
+  // group-major compact K store (compact != 0): k points at the store and
+  // ks_b / ks_h are its sequence / kv-head strides.  The store of one
+  // (sequence, kv head) is a ring per group: group g has kcap[g] key slots
+  // of G elements at element offset koff[g], and key j sits in slot
+  // j % kcap[g], so consecutive keys of a group are contiguous.
+  int compact;
+  int kstore_elems;   // elements of one (sequence, kv head) store
+  int kcap[kMaxGroups];
+  int koff[kMaxGroups];
+};
+
+// Appending keys to the compact K store: token t of row b (position
+// pos0[b] + t) goes, for every group g, to slot (pos0[b] + t) % kcap[g] --
+// unless a later token of the same call takes that slot.
+struct KAppendArgs {
+  const bf16* k;
+  bf16* store;
+  const int* pos0;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t ss_b, ss_h;
+  int B, T, Hkv, d_h, G, ng;
+  int kcap[kMaxGroups];
+  int koff[kMaxGroups];
 };
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s);
+hipError_t launch_kcache_append(const KAppendArgs& a, hipStream_t s);
 
 }  // namespace wp

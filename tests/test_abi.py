@@ -51,6 +51,14 @@ def test_group_cutoffs_clamp_never_prune():
     assert got == [int(v) for v in O.group_cutoffs(1e12, 128, 16, 1e6)]
 
 
+def _i32(vals):
+    return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
 def _ramp_scaled_freqs(theta, d_h, s, lo=0.25, hi=0.75):
     """A per-channel scaled schedule: the first `lo` fraction of channels
     keep their frequency, the last (1 - hi) are divided by s, and the ones in
@@ -110,6 +118,58 @@ def test_general_cutoffs_validation():
     assert L.wp_cutoffs_from_freqs(rev, 64, 2.0, 64, 16, out, 8) == -6
     assert list(out) == [-7] * 8
     assert b"non-decreasing" in L.wp_last_error()
+
+
+def test_kcache_layout_definition_and_printed_table():
+    # group g keeps min(Lmax, D'_g + 1) slots; the cutoffs are the printed
+    # table at theta = 1e6, d_h = 128, G = 16 (28/160/900/5063/28472/...)
+    cut = W.group_cutoffs(1e6, 128, 16)
+    caps, offs = W.kcache_layout(32768, 128, 16, cut)
+    assert caps == [29, 161, 901, 5064, 28473, 32768, 32768, 32768]
+    assert offs == [0] + list(np.cumsum([c * 16 for c in caps]))
+    for Lmax, d, G, cut in [(1, 64, 16, [0, 5, 9, 2**31 - 1]), (1000, 128, 32, [3, 999, 1000, 5000]),
+                            (77, 64, 32, [76, 2**31 - 1])]:
+        caps, offs = W.kcache_layout(Lmax, d, G, cut)
+        assert caps == [min(Lmax, c + 1) for c in cut]
+        assert offs[-1] == sum(c * G for c in caps)
+
+
+def test_kcache_validation_codes():
+    L = W.lib()
+    cut = _i32(W.group_cutoffs(1e4, 128, 16))
+    caps = (ctypes.c_int32 * 8)()
+    offs = (ctypes.c_int64 * 9)()
+    assert L.wp_kcache_layout(100, 128, 16, None, caps, offs) == -1
+    assert L.wp_kcache_layout(0, 128, 16, cut, caps, offs) == -2
+    assert L.wp_kcache_layout(100, 96, 16, cut, caps, offs) == -3
+    bad = _i32([5, 4, 6, 7, 8, 9, 10, 11])
+    assert L.wp_kcache_layout(100, 128, 16, bad, caps, offs) == -6
+    assert L.wp_kcache_layout(100, 128, 16, cut, caps, offs) == 0
+    total = offs[8]
+    F = ctypes.c_void_p(1 << 20)      # never dereferenced: every call below fails validation
+    ks = _i64([4096, 1024, 128])
+    ss = _i64([total * 8, total])
+    assert L.wp_kcache_append(None, 1, 4, 8, 128, ks, F, F, ss, 100, cut, 16, None) == -1
+    assert L.wp_kcache_append(F, 1, 0, 8, 128, ks, F, F, ss, 100, cut, 16, None) == -2
+    assert L.wp_kcache_append(F, 1, 101, 8, 128, ks, F, F, ss, 100, cut, 16, None) == -2   # T > Lmax
+    assert L.wp_kcache_append(F, 1, 4, 8, 128, ks, F, F, _i64([total * 8, total - 16]), 100, cut, 16,
+                              None) == -2                                                    # store stride
+    assert L.wp_kcache_append(F, 1, 4, 8, 128, ks, F, F, _i64([total * 8, total + 4]), 100, cut, 16,
+                              None) == -4                                                    # stride % 8
+    assert L.wp_kcache_append(ctypes.c_void_p((1 << 20) + 8), 1, 4, 8, 128, ks, F, F, ss, 100, cut, 16,
+                              None) == -4
+    assert L.wp_kcache_append(F, 1, 4, 8, 128, ks, F, F, ss, (1 << 24) + 1, cut, 16, None) == -2
+    st9 = _i64([4096, 128, total * 8, total, 1024 * 100, 1024, 128, 4096, 128])
+    args = [F, F, F, F, F, F, 1, 100, 32, 8, 128, st9, cut, 16, 0, F, 1 << 30, 0, None, None]
+    bad_args = list(args)
+    bad_args[17] = 1      # WP_FLAG_DENSE is rejected for the compact store
+    assert L.wp_decode_kcache(*bad_args) == -6
+    bad_args = list(args)
+    bad_args[12] = None   # cutoffs are required
+    assert L.wp_decode_kcache(*bad_args) == -1
+    bad_args = list(args)
+    bad_args[11] = _i64([4096, 128, total * 8, total - 16, 1024 * 100, 1024, 128, 4096, 128])
+    assert L.wp_decode_kcache(*bad_args) == -2
 
 
 def test_tiling_queries():
