@@ -89,6 +89,8 @@ KERNEL_SOURCES = {
                 "rope_positional_encoding_amd/build.py"],
     "decode": ["rope_positional_encoding_amd/csrc/decode.hip", "rope_positional_encoding_amd/csrc/wp_internal.h",
                "rope_positional_encoding_amd/build.py"],
+    "decode_kcache": ["rope_positional_encoding_amd/csrc/decode.hip",
+                      "rope_positional_encoding_amd/csrc/wp_internal.h", "rope_positional_encoding_amd/build.py"],
 }
 
 
@@ -183,12 +185,19 @@ def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
     med = statistics.median(ms)
     k_full = float(kc.numel() * 2)
     k_store = float(store.numel() * 2)
+    avg = sum(ms) / len(ms)
+    ach = dec_alg / (avg * 1e-3) / 1e9
     return {"ms_median": round(med, 4), "ms_min": round(min(ms), 4),
             "algorithmic_gbs": round(dec_alg / (med * 1e-3) / 1e9, 1),
             "k_store_bytes": k_store, "k_cache_bytes": k_full,
             "k_capacity_fraction": round(k_store / k_full, 4),
             "kv_capacity_fraction": round((k_store + k_full) / (2 * k_full), 4),
-            "time_vs_full_cache_decode": round(med / full_ms, 4)}
+            "time_vs_full_cache_decode": round(med / full_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_kcache"),
+                         "algorithmic_bytes": dec_alg,
+                         "kernel": "decode_split_kernel<128,16,compact> + decode_merge_kernel<128>",
+                         "avg_ms": round(avg, 4)}}
 
 
 def main():
