@@ -220,6 +220,60 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, q_pos: int,
     return out
 
 
+def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, dim_cut: np.ndarray):
+    """Gradients of the scalar <dO, O> with respect to q, k and v for the
+    causal WavePrune attention of one sequence (the backward pass that the
+    reading notes' section 2.3 describes for the kernel: the head dimension
+    becomes an output axis, the gradient operands are masked per group, and
+    dQ and dK share one mask).
+
+    q [n, Hq, d_h], k/v [n, Hkv, d_h] (q, k rotated), do [n, Hq, d_h].
+    Plain chain rule through O = softmax(S) V with
+    S_ij = (1/sqrt(d_h)) sum_d keep(i-j, d) q_id k_jd, keep(t, d) = [t <= dim_cut[d]]:
+      dV_j  = sum_i P_ij dO_i
+      dP_ij = dO_i . V_j
+      dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')        (softmax Jacobian)
+      dQ_id = (1/sqrt(d_h)) sum_j dS_ij keep(i-j, d) k_jd
+      dK_jd = (1/sqrt(d_h)) sum_i dS_ij keep(i-j, d) q_id
+    summed over the query heads that share a kv head for dK and dV.  The dims
+    are taken in classes of equal cutoff, each with one n x n mask.
+    Returns dq [n, Hq, d_h], dk [n, Hkv, d_h], dv [n, Hkv, d_h] (float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, Hq, d_h = q.shape
+    Hkv = k.shape[1]
+    r = Hq // Hkv
+    sc = 1.0 / math.sqrt(d_h)
+    cut = np.asarray(dim_cut, dtype=np.int64)
+    dist = np.arange(n)[:, None] - np.arange(n)[None, :]          # i - j
+    causal = dist >= 0
+    classes = [(c, np.nonzero(cut == c)[0]) for c in np.unique(cut)]
+    masks = [(dist <= c) & causal for c, _ in classes]
+    dq = np.zeros_like(q)
+    dk = np.zeros((n, Hkv, d_h))
+    dv = np.zeros((n, Hkv, d_h))
+    for h in range(Hq):
+        kv = h // r
+        S = np.zeros((n, n))
+        for (c, dims), m in zip(classes, masks):
+            S += (q[:, h, dims] @ k[:, kv, dims].T) * m
+        S *= sc
+        S = np.where(causal, S, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dv[:, kv] += P.T @ do[:, h]
+        dP = do[:, h] @ v[:, kv].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        for (c, dims), m in zip(classes, masks):
+            dSm = dS * m
+            dq[:, h, dims] += sc * (dSm @ k[:, kv, dims])
+            dk[:, kv, dims] += sc * (dSm.T @ q[:, h, dims])
+    return dq, dk, dv
+
+
 # ----------------------------------------------------------------------------
 # tile classification
 # ----------------------------------------------------------------------------
