@@ -92,6 +92,8 @@ KERNEL_SOURCES = {
     "decode_kcache": ["rope_positional_encoding_amd/csrc/decode.hip",
                       "rope_positional_encoding_amd/csrc/wp_internal.h", "rope_positional_encoding_amd/build.py"],
 }
+for _srcs in KERNEL_SOURCES.values():
+    _srcs.append("rope_positional_encoding_amd/csrc/wp_device.h")
 
 
 def source_hash(kernel):
@@ -161,6 +163,37 @@ def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512
     }
 
 
+def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops):
+    """wp_prefill_backward at the prefill shape: 1 warmup, median of 3, for
+    the WavePrune table and the dense baseline.  Dense-equivalent work: five
+    d_h-long products per causal pair (S, dP, dV, dK, dQ) = 2.5x the forward."""
+    import torch
+    log("bench: prefill backward")
+    o, lse = W.prefill(q, k, v, cut, G, return_lse=True)
+    od, lsed = W.prefill(q, k, v, None, G, dense=True, return_lse=True)
+    g = torch.randn(q.shape, device=q.device, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(W.lib().wp_prefill_backward_workspace_size(1, n, Hq), dtype=torch.uint8, device=q.device)
+    res = {}
+    for dense in (False, True):
+        oo, ll = (od, lsed) if dense else (o, lse)
+        W.prefill_backward(q, k, v, oo, g, ll, None if dense else cut, G, dense=dense, workspace=ws)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            W.prefill_backward(q, k, v, oo, g, ll, None if dense else cut, G, dense=dense, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res["dense" if dense else "wp"] = statistics.median(ts)
+    bwd_flops = 2.5 * dense_fwd_flops
+    return {"ms_median": round(res["wp"], 3), "dense_ms_median": round(res["dense"], 3),
+            "dense_equiv_tflops": round(bwd_flops / (res["wp"] * 1e-3) / 1e12, 2),
+            "dense_tflops": round(bwd_flops / (res["dense"] * 1e-3) / 1e12, 2),
+            "speedup_vs_dense": round(res["dense"] / res["wp"], 4)}
+
+
 def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
     """The same decode with K read from the group-major compact store (group
     g keeps only its last D'_g + 1 keys): 10 warmups, median of 50."""
@@ -209,6 +242,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kcache", action="store_true", help="skip the compact K store decode line")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches): a kernel of known "
                          "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -362,6 +396,8 @@ def main():
                               "traffic": measured_traffic("decode"), "algorithmic_bytes": dec_alg,
                               "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
                               "avg_ms": round(avg["decode"], 4)}
+    if not args.no_backward:
+        out["prefill_backward"] = bench_backward(W, qr, kr, v, cut, G, n, Hq, d, dense_f)
     if not args.no_kcache:
         out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kc, vc, cl, qp, cut, G, ws, od, dec_alg,
                                             med["decode"])

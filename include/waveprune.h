@@ -160,6 +160,38 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
                      uint32_t flags, int64_t* counters, void* stream);
 
 /*
+ * wp_prefill_backward -- gradients of the scalar <dO, O> of wp_prefill with
+ * respect to q, k and v.
+ *
+ * With P = exp(S - lse) and Dsum_i = dO_i . O_i: dV_j = sum_i P_ij dO_i,
+ * dS_ij = P_ij (dO_i . V_j - Dsum_i), and per group g the same mask as the
+ * forward logit: dQ_i,g = (1/sqrt(d_h)) sum_j [i-j <= D'_g] dS_ij k_j,g,
+ * dK_j,g = (1/sqrt(d_h)) sum_i [i-j <= D'_g] dS_ij q_i,g; dK and dV are
+ * summed over the query heads of a kv head.  The reading notes' section 2.3
+ * (its summary of the paper's Appendix C) describes this backward: the head
+ * dimension becomes an output axis, the gradient operands are masked per
+ * group, and dQ and dK share one mask.  Tiles are classified per group as
+ * in wp_prefill; skipped groups contribute nothing.
+ * q, k, v, o, dout as wp_prefill's q, k, v, o (o = the forward output), lse
+ * the forward's natural-log LSE [B][Hq][n]; dq [B, n, Hq, d_h], dk and dv
+ * [B, n, Hkv, d_h] bf16, written (not accumulated).  strides[24] = {q, k, v,
+ * o, dout, dq, dk, dv} x {batch, token, head} in elements; the q, k, v and
+ * dout token strides must be >= d_h and one sequence of each must span less
+ * than 2^31 bytes.  cutoffs and G as in wp_prefill; flags: WP_FLAG_DENSE or
+ * 0.  workspace: device memory of at least
+ * wp_prefill_backward_workspace_size(B, n, Hq) bytes, 256-byte aligned (the
+ * row sums Dsum).  Asynchronous on stream.
+ */
+wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t n,
+                              int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[24],
+                              const int32_t* cutoffs, int32_t G, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes wp_prefill_backward needs. */
+size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq);
+
+/*
  * wp_decode -- one new query token per sequence against a KV cache.
  *
  * q [B, Hq, d_h] bf16 rotated; k_cache, v_cache [B, Lmax, Hkv, d_h] bf16 (K

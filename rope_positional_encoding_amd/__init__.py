@@ -51,6 +51,9 @@ _SIGNATURES = {
     "wp_kcache_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _I64P, _vp, _vp, _I64P, _i32, _I32P, _i32, _vp]),
     "wp_decode_kcache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P,
                                 _i32, _i32, _vp, _sz, _u32, _vp, _vp]),
+    "wp_prefill_backward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   _I64P, _I32P, _i32, _u32, _vp, _sz, _vp]),
+    "wp_prefill_backward_workspace_size": (_sz, [_i32, _i32, _i32]),
     "wp_decode_num_splits": (_i32, [_i32, _i32, _i32]),
     "wp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "wp_prefill_tiling": (_i32, [_i32, _i32, _I32P, _I32P]),
@@ -235,6 +238,38 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cutoffs: Optional
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, n, Hq, Hkv, d, _i64arr(strides), cut,
         int(G), flags, _ptr(counters), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     dout: torch.Tensor, lse: torch.Tensor, cutoffs: Optional[Sequence[int]], G: int,
+                     dense: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of <dout, o> for wp_prefill's inputs; o and lse
+    [B, Hq, n] (natural log) from the forward pass."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if (tuple(k.shape) != (B, n, Hkv, d) or tuple(v.shape) != (B, n, Hkv, d)
+            or tuple(o.shape) != (B, n, Hq, d) or tuple(dout.shape) != (B, n, Hq, d)):
+        raise ValueError("q/o/dout [B, n, Hq, d_h] and k/v [B, n, Hkv, d_h] must match")
+    if tuple(lse.shape) != (B, Hq, n) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, Hq, n] tensor")
+    need = lib().wp_prefill_backward_workspace_size(B, n, Hq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    strides = []
+    for t in (q, k, v, o, dout, dq, dk, dv):
+        strides += list(t.stride()[:3])
+    cut = None if cutoffs is None else _i32arr(cutoffs)
+    _check(lib().wp_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, n, Hq, Hkv, d, _i64arr(strides), cut, int(G), FLAG_DENSE if dense else 0, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwaveprune.so")
-SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 VALU forms are switched off for all device code.  IEEE mode is

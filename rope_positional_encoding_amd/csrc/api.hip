@@ -456,6 +456,81 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
                      num_splits, workspace, workspace_bytes, flags, counters, stream, false);
 }
 
+size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq) {
+  if (B < 1 || n < 1 || Hq < 1) return 0;
+  return align256((size_t)B * Hq * n * sizeof(float));
+}
+
+wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t n,
+                              int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[24],
+                              const int32_t* cutoffs, int32_t G, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !strides || !workspace)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  if (flags & ~WP_FLAG_DENSE) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
+  const bool dense = flags & WP_FLAG_DENSE;
+  if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (B < 1 || n < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, n, Hq, Hkv must be >= 1");
+  if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WP_ERR_ALIGN, "q, k, v, o, dO, dQ, dK, dV must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(WP_ERR_ALIGN, "lse misaligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(WP_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (wp_status s = check_strides(strides, 24)) return s;
+  // Q, dO (dK/dV kernel) and K, V (dQ kernel) rows are fetched through
+  // buffer resources: token strides >= d_h, one sequence < 2^31 bytes
+  const int tok[4] = {1, 4, 7, 13};
+  for (int t : tok) {
+    if (strides[t] < d_h) return fail(WP_ERR_SHAPE, "q, k, v, dO token strides must be >= d_h");
+    if ((int64_t)(n - 1) * strides[t] * 2 + 2 * d_h >= 2147483647LL)
+      return fail(WP_ERR_SHAPE, "one sequence of q, k, v or dO spans 2^31 bytes or more");
+  }
+  const size_t need = wp_prefill_backward_workspace_size(B, n, Hq);
+  if (workspace_bytes < need)
+    return fail(WP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  const int ng = d_h / G;
+  wp::BackwardArgs a;
+  memset(&a, 0, sizeof(a));
+  if (dense) {
+    for (int g = 0; g < wp::kMaxGroups; ++g) a.cut[g] = WP_NEVER_PRUNE;
+  } else {
+    if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
+    for (int g = 0; g < ng; ++g) a.cut[g] = cutoffs[g];
+  }
+  a.q = static_cast<const wp::bf16*>(q);
+  a.k = static_cast<const wp::bf16*>(k);
+  a.v = static_cast<const wp::bf16*>(v);
+  a.o = static_cast<const wp::bf16*>(o);
+  a.dout = static_cast<const wp::bf16*>(dout);
+  a.lse = lse;
+  a.dsum = static_cast<float*>(workspace);
+  a.dq = static_cast<wp::bf16*>(dq);
+  a.dk = static_cast<wp::bf16*>(dk);
+  a.dv = static_cast<wp::bf16*>(dv);
+  int64_t* st[8][3] = {{&a.qs_b, &a.qs_t, &a.qs_h},    {&a.ks_b, &a.ks_t, &a.ks_h},
+                       {&a.vs_b, &a.vs_t, &a.vs_h},    {&a.os_b, &a.os_t, &a.os_h},
+                       {&a.gs_b, &a.gs_t, &a.gs_h},    {&a.dqs_b, &a.dqs_t, &a.dqs_h},
+                       {&a.dks_b, &a.dks_t, &a.dks_h}, {&a.dvs_b, &a.dvs_t, &a.dvs_h}};
+  for (int t = 0; t < 8; ++t)
+    for (int c = 0; c < 3; ++c) *st[t][c] = strides[3 * t + c];
+  a.B = B; a.n = n; a.Hq = Hq; a.Hkv = Hkv;
+  a.r = Hq / Hkv;
+  a.HPW = (a.r % 4 == 0) ? 4 : (a.r % 2 == 0 ? 2 : 1);
+  a.HG = a.r / a.HPW;
+  a.scale = (float)(1.0 / sqrt((double)d_h));
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
+  if ((long long)B * Hkv * ((n + 31) / 32) * a.HG > 2147483647LL ||
+      (long long)B * n * Hq / 256 + 1 > 2147483647LL)
+    return fail(WP_ERR_SHAPE, "grid too large");
+  hipError_t e = wp::launch_backward(a, d_h, G, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 wp_status wp_kcache_layout(int32_t Lmax, int32_t d_h, int32_t G, const int32_t* cutoffs, int32_t* caps,
                            int64_t* offsets) {
   if (!cutoffs || !caps || !offsets) return fail(WP_ERR_NULL, "cutoffs/caps/offsets is NULL");

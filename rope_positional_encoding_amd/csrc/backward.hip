@@ -1,0 +1,673 @@
+// WavePrune causal attention, backward pass, for gfx950.
+//
+// Gradients of <dO, O> through O = softmax(S) V with the grouped rule
+// S_ij = (1/sqrt(d_h)) sum_g [i - j <= D'_g] q_i,g . k_j,g (WavePrune
+// reading notes on cc.laoqi.cc, section 2.1, Eq. (6), grouped by section 2.3,
+// Eq. (8)).  The same page's kernel paragraph (its summary of the paper's
+// Appendix C) describes the backward: the head dimension becomes an output
+// axis, so the gradient operands are masked per group before the matrix
+// product, and dQ and dK share one mask.  With P = exp(S - LSE) (LSE from the
+// forward pass) and Dsum_i = dO_i . O_i:
+//   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . V_j,   dS_ij = P_ij (dP_ij - Dsum_i),
+//   dQ_i,g = scale sum_j [i-j <= D'_g] dS_ij k_j,g,
+//   dK_j,g = scale sum_i [i-j <= D'_g] dS_ij q_i,g   (and dK, dV summed over
+//   the query heads of a kv head).
+// Every tile is classified per group as in the forward pass; a skipped group
+// contributes to neither dQ nor dK, a full group uses dS as it is, a partial
+// group uses dS masked by distance <= cutoff.
+//
+// gfx950 design:
+//  * Three kernels: row sums Dsum (HBM-bound), a dK/dV kernel whose waves
+//    each own 32 keys and stream the query tiles of every head of their kv
+//    head, and a dQ kernel whose waves each own 32 queries of one head and
+//    stream the key tiles.  No atomics: every output element has one writer.
+//  * All products run on v_mfma_f32_32x32x16_bf16.  In the dK/dV kernel the
+//    logits are computed as S = Q K^T (the lane owns one key column), so P
+//    and dS are already the B operands of dV^T = dO^T P and dK^T = Q^T dS; in
+//    the dQ kernel as S^T = K Q^T (the lane owns one query column), so dS^T
+//    is the B operand of dQ^T = K^T dS^T.  The transposed A operands (dO^T,
+//    Q^T, K^T) come from transposing LDS reads (ds_read_b64_tr_b16) of
+//    row-major tiles, exactly as V^T in the forward pass.
+//  * A tile read both row-wise (16-byte operand reads of 16 rows) and
+//    transposed (transposing reads of 4 rows x 4 chunks) gets one XOR
+//    swizzle of its 16-byte chunks that keeps both read patterns free of
+//    bank conflicts (dual_swz below).
+//  * Group masks of the dK^T / dQ^T products: a 32-row output block covers
+//    one or two groups (G = 32 / 16).  When they are all full the block takes
+//    one MFMA per 16-row k step; otherwise each non-skipped group takes its
+//    own MFMA with the A rows of the other group zeroed and its own (masked)
+//    dS operand.
+#include "wp_device.h"
+#include "wp_internal.h"
+
+namespace wp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+// XOR swizzle of the 16-byte chunks of tile row `row` (bijective on the
+// chunks of a row).  Row-wise reads: 16 lanes read rows R..R+15 at one
+// logical chunk; with 256-byte rows (d_h = 128) every row covers all 64 banks
+// and the swizzle must give the 16 rows distinct chunks; with 128-byte rows
+// two rows share a bank row and the 8 rows of one parity must differ.
+// Transposing reads: 32 lanes read rows R0..R0+3 (R0 % 4 == 0) at logical
+// chunks 4m..4m+3, which must land on 16 distinct chunk positions.
+template <int D>
+__device__ inline int dual_swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+__device__ inline float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Dsum[b][h][i] = sum_d dO[b,i,h,d] * O[b,i,h,d] (float32, bf16 inputs).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BackwardArgs a) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rows = (long long)a.B * a.n * a.Hq;
+  if (idx >= rows) return;
+  const int h = (int)(idx % a.Hq);
+  const long long bi = idx / a.Hq;
+  const int i = (int)(bi % a.n);
+  const int b = (int)(bi / a.n);
+  const bf16* op = a.o + (int64_t)b * a.os_b + (int64_t)i * a.os_t + (int64_t)h * a.os_h;
+  const bf16* gp = a.dout + (int64_t)b * a.gs_b + (int64_t)i * a.gs_t + (int64_t)h * a.gs_h;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(op + 8 * c);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(gp + 8 * c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(bf16_lo(x[w]), bf16_lo(y[w]), acc);
+      acc = __builtin_fmaf(bf16_hi(x[w]), bf16_hi(y[w]), acc);
+    }
+  }
+  a.dsum[((int64_t)b * a.Hq + h) * a.n + i] = acc;
+}
+
+// Classes of a tile from its causal distance range [lD, rD]: groups [0, sL)
+// skip, [sL, sR) partial, [sR, NG) full (cutoffs non-decreasing).
+template <int NG>
+__device__ inline void split_points(const int* cut, int lD, int rD, int& sL, int& sR) {
+  sL = 0;
+  sR = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    sL = (cut[g] < lD) ? g + 1 : sL;
+    sR = (cut[g] < rD) ? g + 1 : sR;
+  }
+  sL = __builtin_amdgcn_readfirstlane(sL);
+  sR = __builtin_amdgcn_readfirstlane(sR);
+}
+
+// Packs a 32x32 output block (this lane's 16 values) into the two B operands
+// of the 16-row k steps that follow (rows 0..15 -> [0], 16..31 -> [1]), in
+// the order the transposing A reads deliver their rows.
+__device__ inline void pack_block(const f32x16& x, u32x4 (&p)[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) p[c][w] = pack_bf16x2(x[8 * c + 2 * w], x[8 * c + 2 * w + 1]);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: a wave owns 32 keys; the workgroup's 4 waves (128 keys) stream the
+// 32-query tiles of every head of their kv head through LDS.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
+  constexpr int NCH = D / 16;
+  constexpr int GC = G / 16;
+  constexpr int NG = D / G;
+  constexpr int ND = D / 32;
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int TILE_B = 32 * RB;                           // one 32-row tile
+  constexpr int LOADS = TILE_B / (kWaves * 64 * 16);
+  static_assert(LOADS >= 1 && TILE_B % (kWaves * 64 * 16) == 0, "tile shape");
+
+  // [stage][Q tile | dO tile], plus the tile's log2-LSE and Dsum rows
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][32];
+  __shared__ __attribute__((aligned(16))) float s_dsum[2][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  bid /= a.Hkv;
+  const int b = bid % a.B;
+  const int kblk = bid / a.B;                      // ascending: most query tiles first
+  const int n = a.n;
+  const int keyw = kblk * 128;                     // first key of the workgroup
+  const int key0 = __builtin_amdgcn_readfirstlane(keyw + 32 * wave);
+  const int key1 = __builtin_amdgcn_readfirstlane(min(n, key0 + 32) - 1);
+  const bool wave_valid = key0 < n;
+
+  // K^T and V^T B operands, resident: lane owns key key0 + l32, dims
+  // [16c + 8hh, +8) of step c
+  u32x4 kr[NCH], vr[NCH];
+  {
+    const int j = key0 + l32;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bf16* kp = a.k + (int64_t)b * a.ks_b + (int64_t)j * a.ks_t + (int64_t)kvh * a.ks_h + hh * 8;
+    const bf16* vp = a.v + (int64_t)b * a.vs_b + (int64_t)j * a.vs_t + (int64_t)kvh * a.vs_h + hh * 8;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      kr[c] = (j < n) ? *reinterpret_cast<const u32x4*>(kp + c * 16) : zero;
+      vr[c] = (j < n) ? *reinterpret_cast<const u32x4*>(vp + c * 16) : zero;
+    }
+  }
+
+  // DMA offsets: load i of this wave fills LDS chunk p = (wave*LOADS+i)*64 +
+  // lane of a tile: row p / CPR, logical chunk (p % CPR) ^ dual_swz(row)
+  const int qrow_b = (int)(a.qs_t * 2);
+  const int grow_b = (int)(a.gs_t * 2);
+  int qoff[LOADS], goff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = (wave * LOADS + i) * 64 + lane;
+    const int row = p / CPR;
+    const int pc = p % CPR;
+    qoff[i] = row * qrow_b + (pc ^ dual_swz<D>(row)) * 16;
+    goff[i] = row * grow_b + (pc ^ dual_swz<D>(row)) * 16;
+  }
+  const float log2e = 1.4426950408889634f;
+  // head hr (0..r-1) of this kv head, query tile starting at i0, into stage st
+  auto load_tile = [&](int hr, int i0, int st) {
+    const int h = kvh * a.r + hr;
+    const int rows = n - i0;
+    const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(
+        a.q + (int64_t)b * a.qs_b + (int64_t)i0 * a.qs_t + (int64_t)h * a.qs_h, (rows - 1) * qrow_b + 2 * D);
+    const __amdgpu_buffer_rsrc_t grs = uniform_rsrc(
+        a.dout + (int64_t)b * a.gs_b + (int64_t)i0 * a.gs_t + (int64_t)h * a.gs_h, (rows - 1) * grow_b + 2 * D);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int dst = (wave * LOADS + i) * 1024;
+      dma16(qrs, &smem[st][dst], qoff[i]);
+      dma16(grs, &smem[st][TILE_B + dst], goff[i]);
+    }
+    if (wave == 0) {
+      // lanes 0-31: log2-domain LSE (+inf past the end: P = 0); 32-63: Dsum
+      const int i = i0 + l32;
+      const int64_t ri = ((int64_t)b * a.Hq + h) * n + i;
+      float val = (hh == 0) ? INFINITY : 0.f;
+      if (i < n) val = (hh == 0) ? a.lse[ri] * log2e : a.dsum[ri];
+      if (hh == 0)
+        s_lse[st][l32] = val;
+      else
+        s_dsum[st][l32] = val;
+    }
+  };
+
+  // row-wise A reads (rows l32 of a tile, logical chunk 2c + hh)
+  int rread[NCH];
+  {
+    const int sw = dual_swz<D>(l32);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) rread[c] = l32 * RB + ((2 * c + hh) ^ sw) * 16;
+  }
+  // transposing A reads: rows 16kc + 4hh + e4 (lo) and + 8 (hi), logical
+  // chunk 4db + 2(group&1) + (q4>>1), half (q4&1); the swizzle of those
+  // rows does not depend on kc
+  const int grp = lane >> 4;
+  const int e4 = (lane & 15) >> 2;
+  const int q4 = lane & 3;
+  int tlo[ND], thi[ND];
+  {
+    const int rlo = 4 * hh + e4, rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int chunk = 4 * db + 2 * (grp & 1) + (q4 >> 1);
+      tlo[db] = rlo * RB + (chunk ^ dual_swz<D>(rlo)) * 16 + (q4 & 1) * 8;
+      thi[db] = rhi * RB + (chunk ^ dual_swz<D>(rhi)) * 16 + (q4 & 1) * 8;
+    }
+  }
+
+  f32x16 dkt[ND], dvt[ND];
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    dkt[db] = zero16;
+    dvt[db] = zero16;
+  }
+  const float sl2 = a.scale_log2;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // tiles: for each head, query tiles from the workgroup's first key on
+  const int t0 = keyw / 32;
+  const int nt = (n + 31) / 32 - t0;               // >= 1 (keyw < n)
+  const int total = a.r * nt;
+  load_tile(0, t0 * 32, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int u = 0; u < total; ++u) {
+    const int st = u & 1;
+    if (u + 1 < total) load_tile((u + 1) / nt, (t0 + (u + 1) % nt) * 32, st ^ 1);
+    const int i0 = (t0 + u % nt) * 32;
+    const int i1 = min(n, i0 + 32) - 1;
+    const unsigned char* sq = &smem[st][0];
+    const unsigned char* sg = &smem[st][TILE_B];
+    if (wave_valid && i1 >= key0) {
+      const int lD = max(0, i0 - key1);
+      const int rD = i1 - key0;
+      int sL, sR;
+      split_points<NG>(a.cut, lD, rD, sL, sR);
+      // rows of this lane's 16 values: queries i0 + out_row(r, hh); the lane's key
+      const int jkey = key0 + l32;
+      auto qop = [&](int c) { return *reinterpret_cast<const u32x4*>(sq + rread[c]); };
+      auto gop = [&](int c) { return *reinterpret_cast<const u32x4*>(sg + rread[c]); };
+
+      // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
+      f32x16 s = zero16;
+      if (sR < NG) {
+        s = mfma32(qop(NCH - 1), kr[NCH - 1], zero16);
+#pragma unroll
+        for (int cc = NCH - 2; cc >= 0; --cc) {
+          if (cc < sR * GC) break;
+          s = mfma32(qop(cc), kr[cc], s);
+        }
+      }
+      if (sL < sR) {
+#pragma unroll
+        for (int g = NG - 1; g >= 0; --g) {
+          if (g >= sR || g < sL) continue;
+          f32x16 t = zero16;
+#pragma unroll
+          for (int c = 0; c < GC; ++c) t = mfma32(qop(g * GC + c), kr[g * GC + c], t);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
+        }
+      }
+      // ---- dP = dO V^T ----
+      f32x16 dp = mfma32(gop(0), vr[0], zero16);
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) dp = mfma32(gop(c), vr[c], dp);
+
+      // ---- P and dS; queries before the key are masked ----
+      f32x16 pm, ds;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = 8 * r4 + 4 * hh;                  // first of 4 consecutive rows
+        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rb]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&s_dsum[st][rb]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const bool keep = i0 + rb + e >= jkey;
+          const float pr = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e])) : 0.f;
+          pm[r] = pr;
+          ds[r] = pr * (dp[r] - dv4[e]);
+        }
+      }
+      u32x4 pp[2], dsp[2];
+      pack_block(pm, pp);
+      pack_block(ds, dsp);
+
+      // ---- dV^T += dO^T P ----
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const u32x2 lo = read_tr16(sg + kc * 16 * RB + tlo[db]);
+          const u32x2 hi = read_tr16(sg + kc * 16 * RB + thi[db]);
+          dvt[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pp[kc], dvt[db]);
+        }
+
+      // ---- dK^T += Q^T dS, masked per group ----
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
+        if (ga >= sR) {                                   // every group of the block full
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
+            const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
+            dkt[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], dkt[db]);
+          }
+        } else {
+#pragma unroll
+          for (int g = ga; g <= gb; ++g) {
+            if (g < sL) continue;                           // skipped: no contribution
+            u32x4 bop[2];
+            if (g >= sR) {
+              bop[0] = dsp[0];
+              bop[1] = dsp[1];
+            } else {
+              f32x16 dm;
+              const int cg = a.cut[g];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
+              pack_block(dm, bop);
+            }
+            const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+              const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
+              const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
+              const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
+              dkt[db] = mfma32(aop, bop[kc], dkt[db]);
+            }
+          }
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- dK = scale * dK^T, dV = dV^T: lane's key, rows = dims ----
+  const int j = key0 + l32;
+  if (wave_valid && j < n) {
+    bf16* kp = a.dk + (int64_t)b * a.dks_b + (int64_t)j * a.dks_t + (int64_t)kvh * a.dks_h + hh * 4;
+    bf16* vp = a.dv + (int64_t)b * a.dvs_b + (int64_t)j * a.dvs_t + (int64_t)kvh * a.dvs_h + hh * 4;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dkt[db][4 * r4] * a.scale, dkt[db][4 * r4 + 1] * a.scale);
+        wk[1] = pack_bf16x2(dkt[db][4 * r4 + 2] * a.scale, dkt[db][4 * r4 + 3] * a.scale);
+        wv[0] = pack_bf16x2(dvt[db][4 * r4], dvt[db][4 * r4 + 1]);
+        wv[1] = pack_bf16x2(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]);
+        *reinterpret_cast<u32x2*>(kp + db * 32 + r4 * 8) = wk;
+        *reinterpret_cast<u32x2*>(vp + db * 32 + r4 * 8) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a wave owns 32 queries of one head (4 waves: HPW heads x 4/HPW query
+// blocks sharing one kv head); the workgroup streams 64-key K / V tiles.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
+  constexpr int NCH = D / 16;
+  constexpr int GC = G / 16;
+  constexpr int NG = D / G;
+  constexpr int ND = D / 32;
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int TILE_B = 64 * RB;
+  constexpr int LOADS = TILE_B / (kWaves * 64 * 16);
+  constexpr int KRB = 256 / RB;
+  static_assert(LOADS >= 1 && TILE_B % (kWaves * 64 * 16) == 0, "tile shape");
+
+  // [stage][K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int QSUB = kWaves / a.HPW;
+  const int QB = 32 * QSUB;
+  const int nqb = (a.n + QB - 1) / QB;
+
+  int bid = blockIdx.x;
+  const int kvh = bid % a.Hkv;
+  bid /= a.Hkv;
+  const int hg = bid % a.HG;
+  bid /= a.HG;
+  const int b = bid % a.B;
+  bid /= a.B;
+  const int qblk = nqb - 1 - bid;                  // heaviest first
+  const int n = a.n;
+  const int h = kvh * a.r + hg * a.HPW + (wave % a.HPW);
+  const int i0_wg = qblk * QB;
+  const int i0w = __builtin_amdgcn_readfirstlane(i0_wg + (wave / a.HPW) * 32);
+  const bool wave_valid = i0w < n;
+  const int i1w = __builtin_amdgcn_readfirstlane(min(n, i0w + 32) - 1);
+  const int kend = min(n, i0_wg + QB);
+  const int nk = __builtin_amdgcn_readfirstlane((kend + 63) / 64);
+
+  // Q^T and dO^T B operands, resident: lane owns query i0w + l32
+  const int qi = i0w + l32;
+  u32x4 qr[NCH], gr[NCH];
+  {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bf16* qp = a.q + (int64_t)b * a.qs_b + (int64_t)qi * a.qs_t + (int64_t)h * a.qs_h + hh * 8;
+    const bf16* gp = a.dout + (int64_t)b * a.gs_b + (int64_t)qi * a.gs_t + (int64_t)h * a.gs_h + hh * 8;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      qr[c] = (qi < n) ? *reinterpret_cast<const u32x4*>(qp + c * 16) : zero;
+      gr[c] = (qi < n) ? *reinterpret_cast<const u32x4*>(gp + c * 16) : zero;
+    }
+  }
+  const float log2e = 1.4426950408889634f;
+  const int64_t rq = ((int64_t)b * a.Hq + h) * n + qi;
+  float lse2 = INFINITY;                           // past the end: P = 0
+  float dsq = 0.f;
+  if (qi < n) {
+    lse2 = a.lse[rq] * log2e;
+    dsq = a.dsum[rq];
+  }
+
+  const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+  const bf16* vbase = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
+  const int krow_b = (int)(a.ks_t * 2);
+  const int vrow_b = (int)(a.vs_t * 2);
+  // K: read row-wise and transposed -> dual swizzle; V: row-wise only ->
+  // swizzle by the row's 256-byte bank row
+  int koff[LOADS], voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = (wave * LOADS + i) * 64 + lane;
+    const int row = p / CPR;
+    const int pc = p % CPR;
+    koff[i] = row * krow_b + (pc ^ dual_swz<D>(row)) * 16;
+    voff[i] = row * vrow_b + (pc ^ ((row / KRB) & (CPR - 1))) * 16;
+  }
+  auto load_tile = [&](int j0, int st) {
+    const int rows = n - j0;
+    const __amdgpu_buffer_rsrc_t krs =
+        uniform_rsrc(kbase + (int64_t)j0 * a.ks_t, (rows - 1) * krow_b + 2 * D);
+    const __amdgpu_buffer_rsrc_t vrs =
+        uniform_rsrc(vbase + (int64_t)j0 * a.vs_t, (rows - 1) * vrow_b + 2 * D);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int dst = (wave * LOADS + i) * 1024;
+      dma16(krs, &smem[st][dst], koff[i]);
+      dma16(vrs, &smem[st][TILE_B + dst], voff[i]);
+    }
+  };
+  // row-wise reads of rows 32kb + l32 (the swizzles of rows 32kb + l32 do not
+  // depend on kb)
+  int kread[NCH], vread[NCH];
+  {
+    const int swk = dual_swz<D>(l32);
+    const int swv = (l32 / KRB) & (CPR - 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      kread[c] = l32 * RB + ((2 * c + hh) ^ swk) * 16;
+      vread[c] = l32 * RB + ((2 * c + hh) ^ swv) * 16;
+    }
+  }
+  // transposing reads of K (rows 16kc + 4hh + e4 and + 8)
+  const int grp = lane >> 4;
+  const int e4 = (lane & 15) >> 2;
+  const int q4 = lane & 3;
+  int tlo[ND], thi[ND];
+  {
+    const int rlo = 4 * hh + e4, rhi = rlo + 8;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int chunk = 4 * db + 2 * (grp & 1) + (q4 >> 1);
+      tlo[db] = rlo * RB + (chunk ^ dual_swz<D>(rlo)) * 16 + (q4 & 1) * 8;
+      thi[db] = rhi * RB + (chunk ^ dual_swz<D>(rhi)) * 16 + (q4 & 1) * 8;
+    }
+  }
+
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  f32x16 dqt[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) dqt[db] = zero16;
+  const float sl2 = a.scale_log2;
+
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int it = 0; it < nk; ++it) {
+    const int j0 = it * 64;
+    const int st = it & 1;
+    if (it + 1 < nk) load_tile(j0 + 64, st ^ 1);
+    const unsigned char* sk = &smem[st][0];
+    const unsigned char* sv = &smem[st][TILE_B];
+    if (wave_valid && j0 <= i1w) {
+      const int j1 = min(n - 1, j0 + 63);
+      int sL, sR;
+      split_points<NG>(a.cut, max(0, i0w - j1), i1w - j0, sL, sR);
+      auto kop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c]); };
+      auto vop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sv + kb * 32 * RB + vread[c]); };
+      const int base = qi - j0;                    // distance = base - (32kb + out_row(r))
+
+      u32x4 dsp[4];                                // dS^T as B operands, 16 keys each
+      f32x16 dsv[2];                               // dS^T values (for partial-group masks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // ---- S^T = K Q^T: full groups as one chain, then partials ----
+        f32x16 s = zero16;
+        if (sR < NG) {
+          s = mfma32(kop(kb, NCH - 1), qr[NCH - 1], zero16);
+#pragma unroll
+          for (int cc = NCH - 2; cc >= 0; --cc) {
+            if (cc < sR * GC) break;
+            s = mfma32(kop(kb, cc), qr[cc], s);
+          }
+        }
+        if (sL < sR) {
+#pragma unroll
+          for (int g = NG - 1; g >= 0; --g) {
+            if (g >= sR || g < sL) continue;
+            f32x16 t = zero16;
+#pragma unroll
+            for (int c = 0; c < GC; ++c) t = mfma32(kop(kb, g * GC + c), qr[g * GC + c], t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] += (base - 32 * kb - out_row(r, hh) <= a.cut[g]) ? t[r] : 0.f;
+          }
+        }
+        // ---- dP^T = V dO^T ----
+        f32x16 dp = mfma32(vop(kb, 0), gr[0], zero16);
+#pragma unroll
+        for (int c = 1; c < NCH; ++c) dp = mfma32(vop(kb, c), gr[c], dp);
+        // ---- P^T, dS^T; keys after the query are masked ----
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool keep = base - 32 * kb - out_row(r, hh) >= 0;
+          const float pr = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2)) : 0.f;
+          dsv[kb][r] = pr * (dp[r] - dsq);
+        }
+        u32x4 pk[2];
+        pack_block(dsv[kb], pk);
+        dsp[2 * kb] = pk[0];
+        dsp[2 * kb + 1] = pk[1];
+      }
+
+      // ---- dQ^T += K^T dS^T, masked per group ----
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
+        if (ga >= sR) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const u32x2 lo = read_tr16(sk + kc * 16 * RB + tlo[db]);
+            const u32x2 hi = read_tr16(sk + kc * 16 * RB + thi[db]);
+            dqt[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], dqt[db]);
+          }
+        } else {
+#pragma unroll
+          for (int g = ga; g <= gb; ++g) {
+            if (g < sL) continue;
+            u32x4 bop[4];
+            if (g >= sR) {
+#pragma unroll
+              for (int kc = 0; kc < 4; ++kc) bop[kc] = dsp[kc];
+            } else {
+              const int cg = a.cut[g];
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) {
+                f32x16 dm;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  dm[r] = (base - 32 * kb - out_row(r, hh) <= cg) ? dsv[kb][r] : 0.f;
+                u32x4 pk[2];
+                pack_block(dm, pk);
+                bop[2 * kb] = pk[0];
+                bop[2 * kb + 1] = pk[1];
+              }
+            }
+            const bool mine = ((32 * db + l32) / G) == g;
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+              const u32x2 lo = read_tr16(sk + kc * 16 * RB + tlo[db]);
+              const u32x2 hi = read_tr16(sk + kc * 16 * RB + thi[db]);
+              const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
+              dqt[db] = mfma32(aop, bop[kc], dqt[db]);
+            }
+          }
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- dQ = scale * dQ^T: lane's query, rows = dims ----
+  if (wave_valid && qi < n) {
+    bf16* qp = a.dq + (int64_t)b * a.dqs_b + (int64_t)qi * a.dqs_t + (int64_t)h * a.dqs_h + hh * 4;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dqt[db][4 * r4] * a.scale, dqt[db][4 * r4 + 1] * a.scale);
+        w[1] = pack_bf16x2(dqt[db][4 * r4 + 2] * a.scale, dqt[db][4 * r4 + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(qp + db * 32 + r4 * 8) = w;
+      }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
+  const long long rows = (long long)a.B * a.n * a.Hq;
+  hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long kblocks = (long long)a.Hkv * a.B * ((a.n + 127) / 128);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kblocks), dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int QB = 32 * (kWaves / a.HPW);
+  const long long qblocks = (long long)a.Hkv * a.HG * a.B * ((a.n + QB - 1) / QB);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)qblocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, int d_h, int G, hipStream_t s) {
+  if (a.B < 1 || a.n < 1) return hipSuccess;
+  if (d_h == 128 && G == 16) return launch_bwd<128, 16>(a, s);
+  if (d_h == 128 && G == 32) return launch_bwd<128, 32>(a, s);
+  if (d_h == 64 && G == 16) return launch_bwd<64, 16>(a, s);
+  if (d_h == 64 && G == 32) return launch_bwd<64, 32>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace wp

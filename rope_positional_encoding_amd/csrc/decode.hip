@@ -24,6 +24,7 @@
 //    (keys permuted to match), so the A operand is one 16-byte LDS read.
 //  * The 4 waves merge through LDS at the end; a second kernel merges the
 //    splits (log-sum-exp weighted), one wave per (sequence, query head).
+#include "wp_device.h"
 #include "wp_internal.h"
 
 namespace wp {
@@ -36,27 +37,6 @@ constexpr int kWaves = 4;
 __device__ inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> packed bf16 pair (nearest even), one v_cvt_pk_bf16_f32
-__device__ inline unsigned int pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-
-// dword 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts
-constexpr int kBufferFlags = 0x00020000;
-
-// A raw buffer resource for [p, p + bytes) in scalar registers (base and size
-// are wave-uniform; readfirstlane makes that explicit for the compiler).
-__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
 }
 
 // Position of key-quad kq (keys 4kq..4kq+3 of a 32-key block) inside the

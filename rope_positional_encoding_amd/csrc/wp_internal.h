@@ -103,9 +103,38 @@ struct KAppendArgs {
   int koff[kMaxGroups];
 };
 
+// Backward pass of prefill (gradients of <dO, O>).
+struct BackwardArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;    // [B][Hq][n], natural log, from the forward pass
+  float* dsum;         // [B][Hq][n] workspace: rowsum(dO * O)
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int64_t gs_b, gs_t, gs_h;      // dO
+  int64_t dqs_b, dqs_t, dqs_h;
+  int64_t dks_b, dks_t, dks_h;
+  int64_t dvs_b, dvs_t, dvs_h;
+  int B, n, Hq, Hkv;
+  int r;          // Hq / Hkv
+  int HPW, HG;    // dQ kernel: query heads per workgroup, head groups per kv head
+  float scale;        // 1 / sqrt(d_h)
+  float scale_log2;   // log2(e) / sqrt(d_h)
+  int cut[kMaxGroups];
+};
+
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_kcache_append(const KAppendArgs& a, hipStream_t s);
+hipError_t launch_backward(const BackwardArgs& a, int d_h, int G, hipStream_t s);
 
 }  // namespace wp
