@@ -117,11 +117,24 @@ __device__ inline void pack_block(const f32x16& x, u32x4 (&p)[2]) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: a wave owns 32 keys; the workgroup's 4 waves (128 keys) stream the
-// 32-query tiles of every head of their kv head through LDS.
+// dK / dV.  A workgroup owns 128 keys of one kv head and streams the 32-query
+// tiles of every query head of that kv head.  Its 8 waves work in pairs;
+// pair p owns keys keyw + 32p .. +31:
+//  * wave p (K^T resident) forms S = Q K^T and P for tile u, hands P to its
+//    partner through LDS and accumulates dV^T += dO^T P;
+//  * wave 4 + p (V^T resident) takes tile u one step later: dP = dO V^T,
+//    dS = P (dP - Dsum), dK^T += Q^T dS.
+// Each wave then holds one 32x128 accumulator and one resident operand,
+// which keeps it under 256 registers: the two waves of a SIMD overlap one's
+// exponentials with the other's MFMAs.  Tiles stream through three LDS
+// stages: tile u + 1 loads during step u, while the first waves of the pairs
+// use tile u and the second waves tile u - 1.
 // ---------------------------------------------------------------------------
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = 64 * kKvWaves;
+
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int NCH = D / 16;
   constexpr int GC = G / 16;
   constexpr int NG = D / G;
@@ -129,17 +142,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int TILE_B = 32 * RB;                           // one 32-row tile
-  constexpr int LOADS = TILE_B / (kWaves * 64 * 16);
-  static_assert(LOADS >= 1 && TILE_B % (kWaves * 64 * 16) == 0, "tile shape");
+  constexpr int TCH = TILE_B / 16;                          // its 16-byte chunks
+  constexpr int NL = 2 * TCH / kKvThreads;                  // DMA loads per lane and tile
+  static_assert(NL >= 1 && (2 * TCH) % kKvThreads == 0 && TCH % 64 == 0, "tile shape");
 
-  // [stage][Q tile | dO tile], plus the tile's log2-LSE and Dsum rows
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][32];
-  __shared__ __attribute__((aligned(16))) float s_dsum[2][32];
+  // [stage][Q tile | dO tile]; the tile's log2-LSE and Dsum rows; P of each
+  // pair, float, [parity][pair][r / 4][lane][r % 4]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[3][2 * TILE_B];
+  __shared__ __attribute__((aligned(16))) float s_lse[3][32];
+  __shared__ __attribute__((aligned(16))) float s_dsum[3][32];
+  __shared__ __attribute__((aligned(16))) float s_p[2][4][16 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool pwave = wave < 4;                     // forms P and dV (else dP, dS, dK)
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -150,37 +168,35 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   const int kblk = bid / a.B;                      // ascending: most query tiles first
   const int n = a.n;
   const int keyw = kblk * 128;                     // first key of the workgroup
-  const int key0 = __builtin_amdgcn_readfirstlane(keyw + 32 * wave);
+  const int key0 = __builtin_amdgcn_readfirstlane(keyw + 32 * pair);
   const int key1 = __builtin_amdgcn_readfirstlane(min(n, key0 + 32) - 1);
   const bool wave_valid = key0 < n;
 
-  // K^T and V^T B operands, resident: lane owns key key0 + l32, dims
+  // the resident B operand, K^T or V^T: lane owns key key0 + l32, dims
   // [16c + 8hh, +8) of step c
-  u32x4 kr[NCH], vr[NCH];
+  u32x4 br[NCH];
   {
     const int j = key0 + l32;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bf16* kp = a.k + (int64_t)b * a.ks_b + (int64_t)j * a.ks_t + (int64_t)kvh * a.ks_h + hh * 8;
-    const bf16* vp = a.v + (int64_t)b * a.vs_b + (int64_t)j * a.vs_t + (int64_t)kvh * a.vs_h + hh * 8;
+    const bf16* p = pwave ? a.k + (int64_t)b * a.ks_b + (int64_t)j * a.ks_t + (int64_t)kvh * a.ks_h
+                          : a.v + (int64_t)b * a.vs_b + (int64_t)j * a.vs_t + (int64_t)kvh * a.vs_h;
+    p += hh * 8;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      kr[c] = (j < n) ? *reinterpret_cast<const u32x4*>(kp + c * 16) : zero;
-      vr[c] = (j < n) ? *reinterpret_cast<const u32x4*>(vp + c * 16) : zero;
-    }
+    for (int c = 0; c < NCH; ++c) br[c] = (j < n) ? *reinterpret_cast<const u32x4*>(p + c * 16) : zero;
   }
 
-  // DMA offsets: load i of this wave fills LDS chunk p = (wave*LOADS+i)*64 +
-  // lane of a tile: row p / CPR, logical chunk (p % CPR) ^ dual_swz(row)
+  // DMA: load i of this lane fills chunk p = wave*64 + lane + i*512 of a
+  // stage ([Q | dO], TCH chunks each): tile row pt / CPR, logical chunk
+  // (pt % CPR) ^ dual_swz(row), pt = p % TCH
   const int qrow_b = (int)(a.qs_t * 2);
   const int grow_b = (int)(a.gs_t * 2);
-  int qoff[LOADS], goff[LOADS];
+  int doff[NL];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = (wave * LOADS + i) * 64 + lane;
-    const int row = p / CPR;
-    const int pc = p % CPR;
-    qoff[i] = row * qrow_b + (pc ^ dual_swz<D>(row)) * 16;
-    goff[i] = row * grow_b + (pc ^ dual_swz<D>(row)) * 16;
+  for (int i = 0; i < NL; ++i) {
+    const int p = wave * 64 + lane + kKvThreads * i;
+    const int pt = p % TCH;
+    const int row = pt / CPR;
+    doff[i] = row * (p < TCH ? qrow_b : grow_b) + ((pt % CPR) ^ dual_swz<D>(row)) * 16;
   }
   const float log2e = 1.4426950408889634f;
   // head hr (0..r-1) of this kv head, query tile starting at i0, into stage st
@@ -192,10 +208,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     const __amdgpu_buffer_rsrc_t grs = uniform_rsrc(
         a.dout + (int64_t)b * a.gs_b + (int64_t)i0 * a.gs_t + (int64_t)h * a.gs_h, (rows - 1) * grow_b + 2 * D);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int dst = (wave * LOADS + i) * 1024;
-      dma16(qrs, &smem[st][dst], qoff[i]);
-      dma16(grs, &smem[st][TILE_B + dst], goff[i]);
+    for (int i = 0; i < NL; ++i) {
+      const int p0 = wave * 64 + kKvThreads * i;  // wave-uniform: Q or dO
+      dma16(p0 < TCH ? qrs : grs, &smem[st][p0 * 16], doff[i]);
     }
     if (wave == 0) {
       // lanes 0-31: log2-domain LSE (+inf past the end: P = 0); 32-63: Dsum
@@ -234,15 +249,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     }
   }
 
-  f32x16 dkt[ND], dvt[ND];
+  // dV^T (first wave of a pair) or dK^T (second): rows dims, columns keys
+  f32x16 acc[ND];
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int db = 0; db < ND; ++db) {
-    dkt[db] = zero16;
-    dvt[db] = zero16;
-  }
+  for (int db = 0; db < ND; ++db) acc[db] = zero16;
   const float sl2 = a.scale_log2;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int jkey = key0 + l32;                     // this lane's key
 
   // tiles: for each head, query tiles from the workgroup's first key on
   const int t0 = keyw / 32;
@@ -252,114 +266,128 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int u = 0; u < total; ++u) {
-    const int st = u & 1;
-    if (u + 1 < total) load_tile((u + 1) / nt, (t0 + (u + 1) % nt) * 32, st ^ 1);
-    const int i0 = (t0 + u % nt) * 32;
+  for (int u = 0; u <= total; ++u) {
+    if (u + 1 < total) load_tile((u + 1) / nt, (t0 + (u + 1) % nt) * 32, (u + 1) % 3);
+    // first waves: tile u; second waves: tile u - 1
+    const int v = pwave ? u : u - 1;
+    const int i0 = (t0 + v % nt) * 32;
     const int i1 = min(n, i0 + 32) - 1;
+    const int st = v % 3;
     const unsigned char* sq = &smem[st][0];
     const unsigned char* sg = &smem[st][TILE_B];
-    if (wave_valid && i1 >= key0) {
+    float* pbuf = &s_p[v & 1][pair][0];
+    if (v >= 0 && v < total && wave_valid && i1 >= key0) {
       const int lD = max(0, i0 - key1);
       const int rD = i1 - key0;
       int sL, sR;
       split_points<NG>(a.cut, lD, rD, sL, sR);
-      // rows of this lane's 16 values: queries i0 + out_row(r, hh); the lane's key
-      const int jkey = key0 + l32;
-      auto qop = [&](int c) { return *reinterpret_cast<const u32x4*>(sq + rread[c]); };
-      auto gop = [&](int c) { return *reinterpret_cast<const u32x4*>(sg + rread[c]); };
-
-      // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
-      f32x16 s = zero16;
-      if (sR < NG) {
-        s = mfma32(qop(NCH - 1), kr[NCH - 1], zero16);
+      auto rop = [&](const unsigned char* t, int c) { return *reinterpret_cast<const u32x4*>(t + rread[c]); };
+      if (pwave) {
+        // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
+        f32x16 s = zero16;
+        if (sR < NG) {
+          s = mfma32(rop(sq, NCH - 1), br[NCH - 1], zero16);
 #pragma unroll
-        for (int cc = NCH - 2; cc >= 0; --cc) {
-          if (cc < sR * GC) break;
-          s = mfma32(qop(cc), kr[cc], s);
+          for (int cc = NCH - 2; cc >= 0; --cc) {
+            if (cc < sR * GC) break;
+            s = mfma32(rop(sq, cc), br[cc], s);
+          }
         }
-      }
-      if (sL < sR) {
+        if (sL < sR) {
 #pragma unroll
-        for (int g = NG - 1; g >= 0; --g) {
-          if (g >= sR || g < sL) continue;
-          f32x16 t = zero16;
+          for (int g = NG - 1; g >= 0; --g) {
+            if (g >= sR || g < sL) continue;
+            f32x16 t = zero16;
 #pragma unroll
-          for (int c = 0; c < GC; ++c) t = mfma32(qop(g * GC + c), kr[g * GC + c], t);
+            for (int c = 0; c < GC; ++c) t = mfma32(rop(sq, g * GC + c), br[g * GC + c], t);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
+            for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
+          }
         }
-      }
-      // ---- dP = dO V^T ----
-      f32x16 dp = mfma32(gop(0), vr[0], zero16);
+        // ---- P (queries before the key masked), to the partner and packed ----
+        f32x16 pm;
 #pragma unroll
-      for (int c = 1; c < NCH; ++c) dp = mfma32(gop(c), vr[c], dp);
-
-      // ---- P and dS; queries before the key are masked ----
-      f32x16 pm, ds;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = 8 * r4 + 4 * hh;                // first of 4 consecutive rows
+          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rb]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          float4 p4;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rb = 8 * r4 + 4 * hh;                  // first of 4 consecutive rows
-        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rb]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s_dsum[st][rb]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const bool keep = i0 + rb + e >= jkey;
-          const float pr = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e])) : 0.f;
-          pm[r] = pr;
-          ds[r] = pr * (dp[r] - dv4[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const bool keep = i0 + rb + e >= jkey;
+            pm[r] = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e])) : 0.f;
+          }
+          p4.x = pm[4 * r4];
+          p4.y = pm[4 * r4 + 1];
+          p4.z = pm[4 * r4 + 2];
+          p4.w = pm[4 * r4 + 3];
+          *reinterpret_cast<float4*>(pbuf + (r4 * 64 + lane) * 4) = p4;
         }
-      }
-      u32x4 pp[2], dsp[2];
-      pack_block(pm, pp);
-      pack_block(ds, dsp);
-
-      // ---- dV^T += dO^T P ----
+        u32x4 pp[2];
+        pack_block(pm, pp);
+        // ---- dV^T += dO^T P ----
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+          for (int db = 0; db < ND; ++db) {
+            const u32x2 lo = read_tr16(sg + kc * 16 * RB + tlo[db]);
+            const u32x2 hi = read_tr16(sg + kc * 16 * RB + thi[db]);
+            acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pp[kc], acc[db]);
+          }
+      } else {
+        // ---- dP = dO V^T ----
+        f32x16 dp = mfma32(rop(sg, 0), br[0], zero16);
+#pragma unroll
+        for (int c = 1; c < NCH; ++c) dp = mfma32(rop(sg, c), br[c], dp);
+        // ---- dS = P (dP - Dsum), P from the partner ----
+        f32x16 ds;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = 8 * r4 + 4 * hh;
+          const float4 d4 = *reinterpret_cast<const float4*>(&s_dsum[st][rb]);
+          const float4 p4 = *reinterpret_cast<const float4*>(pbuf + (r4 * 64 + lane) * 4);
+          ds[4 * r4] = p4.x * (dp[4 * r4] - d4.x);
+          ds[4 * r4 + 1] = p4.y * (dp[4 * r4 + 1] - d4.y);
+          ds[4 * r4 + 2] = p4.z * (dp[4 * r4 + 2] - d4.z);
+          ds[4 * r4 + 3] = p4.w * (dp[4 * r4 + 3] - d4.w);
+        }
+        u32x4 dsp[2];
+        pack_block(ds, dsp);
+        // ---- dK^T += Q^T dS, masked per group ----
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const u32x2 lo = read_tr16(sg + kc * 16 * RB + tlo[db]);
-          const u32x2 hi = read_tr16(sg + kc * 16 * RB + thi[db]);
-          dvt[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pp[kc], dvt[db]);
-        }
-
-      // ---- dK^T += Q^T dS, masked per group ----
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
-        if (ga >= sR) {                                   // every group of the block full
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
-            const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-            dkt[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], dkt[db]);
-          }
-        } else {
-#pragma unroll
-          for (int g = ga; g <= gb; ++g) {
-            if (g < sL) continue;                           // skipped: no contribution
-            u32x4 bop[2];
-            if (g >= sR) {
-              bop[0] = dsp[0];
-              bop[1] = dsp[1];
-            } else {
-              f32x16 dm;
-              const int cg = a.cut[g];
-#pragma unroll
-              for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
-              pack_block(dm, bop);
-            }
-            const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
+          const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
+          if (ga >= sR) {                                 // every group of the block full
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
               const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
               const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-              const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
-              dkt[db] = mfma32(aop, bop[kc], dkt[db]);
+              acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], acc[db]);
+            }
+          } else {
+#pragma unroll
+            for (int g = ga; g <= gb; ++g) {
+              if (g < sL) continue;                         // skipped: no contribution
+              u32x4 bop[2];
+              if (g >= sR) {
+                bop[0] = dsp[0];
+                bop[1] = dsp[1];
+              } else {
+                f32x16 dm;
+                const int cg = a.cut[g];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
+                pack_block(dm, bop);
+              }
+              const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
+#pragma unroll
+              for (int kc = 0; kc < 2; ++kc) {
+                const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
+                const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
+                const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
+                acc[db] = mfma32(aop, bop[kc], acc[db]);
+              }
             }
           }
         }
@@ -369,22 +397,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     __syncthreads();
   }
 
-  // ---- dK = scale * dK^T, dV = dV^T: lane's key, rows = dims ----
-  const int j = key0 + l32;
-  if (wave_valid && j < n) {
-    bf16* kp = a.dk + (int64_t)b * a.dks_b + (int64_t)j * a.dks_t + (int64_t)kvh * a.dks_h + hh * 4;
-    bf16* vp = a.dv + (int64_t)b * a.dvs_b + (int64_t)j * a.dvs_t + (int64_t)kvh * a.dvs_h + hh * 4;
+  // ---- dV = dV^T (first waves), dK = scale * dK^T (second): lane's key,
+  // rows = dims ----
+  if (wave_valid && jkey < n) {
+    const float sc = pwave ? 1.f : a.scale;
+    bf16* op = pwave ? a.dv + (int64_t)b * a.dvs_b + (int64_t)jkey * a.dvs_t + (int64_t)kvh * a.dvs_h
+                     : a.dk + (int64_t)b * a.dks_b + (int64_t)jkey * a.dks_t + (int64_t)kvh * a.dks_h;
+    op += hh * 4;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dkt[db][4 * r4] * a.scale, dkt[db][4 * r4 + 1] * a.scale);
-        wk[1] = pack_bf16x2(dkt[db][4 * r4 + 2] * a.scale, dkt[db][4 * r4 + 3] * a.scale);
-        wv[0] = pack_bf16x2(dvt[db][4 * r4], dvt[db][4 * r4 + 1]);
-        wv[1] = pack_bf16x2(dvt[db][4 * r4 + 2], dvt[db][4 * r4 + 3]);
-        *reinterpret_cast<u32x2*>(kp + db * 32 + r4 * 8) = wk;
-        *reinterpret_cast<u32x2*>(vp + db * 32 + r4 * 8) = wv;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[db][4 * r4] * sc, acc[db][4 * r4 + 1] * sc);
+        w[1] = pack_bf16x2(acc[db][4 * r4 + 2] * sc, acc[db][4 * r4 + 3] * sc);
+        *reinterpret_cast<u32x2*>(op + db * 32 + r4 * 8) = w;
       }
   }
 }
@@ -650,7 +677,7 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long kblocks = (long long)a.Hkv * a.B * ((a.n + 127) / 128);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kblocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kblocks), dim3(kKvThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int QB = 32 * (kWaves / a.HPW);
