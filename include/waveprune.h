@@ -179,8 +179,9 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
  * dout token strides must be >= d_h and one sequence of each must span less
  * than 2^31 bytes.  cutoffs and G as in wp_prefill; flags: WP_FLAG_DENSE or
  * 0.  workspace: device memory of at least
- * wp_prefill_backward_workspace_size(B, n, Hq) bytes, 256-byte aligned (the
- * row sums Dsum).  Asynchronous on stream.
+ * wp_prefill_backward_workspace_size(B, n, Hq) bytes, 256-byte aligned (two
+ * floats per query row: its LSE in base 2 and its row sum Dsum).
+ * Asynchronous on stream.
  */
 wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, void* dq, void* dk, void* dv, int32_t B, int32_t n,

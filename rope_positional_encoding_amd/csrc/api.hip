@@ -458,7 +458,7 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
 
 size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq) {
   if (B < 1 || n < 1 || Hq < 1) return 0;
-  return align256((size_t)B * Hq * n * sizeof(float));
+  return align256((size_t)B * Hq * n * 2 * sizeof(float));
 }
 
 wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -507,7 +507,7 @@ wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const
   a.o = static_cast<const wp::bf16*>(o);
   a.dout = static_cast<const wp::bf16*>(dout);
   a.lse = lse;
-  a.dsum = static_cast<float*>(workspace);
+  a.rowv = static_cast<float*>(workspace);
   a.dq = static_cast<wp::bf16*>(dq);
   a.dk = static_cast<wp::bf16*>(dk);
   a.dv = static_cast<wp::bf16*>(dv);

@@ -44,9 +44,6 @@ namespace wp {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-
 // XOR swizzle of the 16-byte chunks of tile row `row` (bijective on the
 // chunks of a row).  Row-wise reads: 16 lanes read rows R..R+15 at one
 // logical chunk; with 256-byte rows (d_h = 128) every row covers all 64 banks
@@ -65,7 +62,8 @@ __device__ inline int dual_swz(int row) {
 __device__ inline float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Dsum[b][h][i] = sum_d dO[b,i,h,d] * O[b,i,h,d] (float32, bf16 inputs).
+// Row values of query i of head h: its LSE in base 2 and Dsum[b][h][i] =
+// sum_d dO[b,i,h,d] * O[b,i,h,d] (float32, bf16 inputs), stored as a pair.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BackwardArgs a) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -88,7 +86,8 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BackwardArgs a) {
       acc = __builtin_fmaf(bf16_hi(x[w]), bf16_hi(y[w]), acc);
     }
   }
-  a.dsum[((int64_t)b * a.Hq + h) * a.n + i] = acc;
+  const int64_t r = ((int64_t)b * a.Hq + h) * a.n + i;
+  *reinterpret_cast<float2*>(a.rowv + 2 * r) = float2{a.lse[r] * 1.4426950408889634f, acc};
 }
 
 // Classes of a tile from its causal distance range [lD, rD]: groups [0, sL)
@@ -126,12 +125,25 @@ __device__ inline void pack_block(const f32x16& x, u32x4 (&p)[2]) {
 //    dS = P (dP - Dsum), dK^T += Q^T dS.
 // Each wave then holds one 32x128 accumulator and one resident operand,
 // which keeps it under 256 registers: the two waves of a SIMD overlap one's
-// exponentials with the other's MFMAs.  Tiles stream through three LDS
-// stages: tile u + 1 loads during step u, while the first waves of the pairs
-// use tile u and the second waves tile u - 1.
+// exponentials with the other's MFMAs.  Tiles (Q, dO and the rows' LSE and
+// Dsum) arrive by DMA kPrefetch steps ahead of the first waves' use.
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kPrefetch = 1;                      // tiles in flight ahead of use
+constexpr int kStages = kPrefetch + 2;            // + the tiles of both halves of a pair
+
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+// Barrier without the fence of __syncthreads, which would wait for every DMA
+// in flight; callers wait for what they need first.
+__device__ inline void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
@@ -146,11 +158,10 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int NL = 2 * TCH / kKvThreads;                  // DMA loads per lane and tile
   static_assert(NL >= 1 && (2 * TCH) % kKvThreads == 0 && TCH % 64 == 0, "tile shape");
 
-  // [stage][Q tile | dO tile]; the tile's log2-LSE and Dsum rows; P of each
-  // pair, float, [parity][pair][r / 4][lane][r % 4]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[3][2 * TILE_B];
-  __shared__ __attribute__((aligned(16))) float s_lse[3][32];
-  __shared__ __attribute__((aligned(16))) float s_dsum[3][32];
+  // [stage][Q tile | dO tile]; the rows' (log2 LSE, Dsum) pairs per stage;
+  // P of each pair, float, [parity][pair][r / 4][lane][r % 4]
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2 * TILE_B];
+  __shared__ __attribute__((aligned(256))) float s_ld[kStages][64];
   __shared__ __attribute__((aligned(16))) float s_p[2][4][16 * 64];
 
   const int tid = threadIdx.x;
@@ -161,11 +172,12 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // block decomposition, kept scalar (the divisions run on the vector unit)
   int bid = blockIdx.x;
-  const int kvh = bid % a.Hkv;
+  const int kvh = __builtin_amdgcn_readfirstlane(bid % a.Hkv);
   bid /= a.Hkv;
-  const int b = bid % a.B;
-  const int kblk = bid / a.B;                      // ascending: most query tiles first
+  const int b = __builtin_amdgcn_readfirstlane(bid % a.B);
+  const int kblk = __builtin_amdgcn_readfirstlane(bid / a.B);   // ascending: most query tiles first
   const int n = a.n;
   const int keyw = kblk * 128;                     // first key of the workgroup
   const int key0 = __builtin_amdgcn_readfirstlane(keyw + 32 * pair);
@@ -198,10 +210,18 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     const int row = pt / CPR;
     doff[i] = row * (p < TCH ? qrow_b : grow_b) + ((pt % CPR) ^ dual_swz<D>(row)) * 16;
   }
-  const float log2e = 1.4426950408889634f;
-  // head hr (0..r-1) of this kv head, query tile starting at i0, into stage st
-  auto load_tile = [&](int hr, int i0, int st) {
+  // Tiles t = 0 .. total-1: head hr = t / nt of this kv head, queries from
+  // (t0 + ti) * 32, ti = t % nt.  Head and tile index are stepped as scalar
+  // counters (an integer division would run on the vector unit).
+  const int t0 = keyw / 32;
+  const int nt = __builtin_amdgcn_readfirstlane((n + 31) / 32 - t0);   // >= 1 (keyw < n)
+  const int total = a.r * nt;
+  // tile (hr, ti): its Q / dO rows go to dst, its 32 row pairs to ldst
+  // (wave 0, lanes 0-15, 16 bytes each; rows past the end read as zero and
+  // are masked)
+  auto load_tile = [&](int hr, int ti, unsigned char* dst, float* ldst) {
     const int h = kvh * a.r + hr;
+    const int i0 = (t0 + ti) * 32;
     const int rows = n - i0;
     const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(
         a.q + (int64_t)b * a.qs_b + (int64_t)i0 * a.qs_t + (int64_t)h * a.qs_h, (rows - 1) * qrow_b + 2 * D);
@@ -210,19 +230,10 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int p0 = wave * 64 + kKvThreads * i;  // wave-uniform: Q or dO
-      dma16(p0 < TCH ? qrs : grs, &smem[st][p0 * 16], doff[i]);
+      dma16(p0 < TCH ? qrs : grs, dst + p0 * 16, doff[i]);
     }
-    if (wave == 0) {
-      // lanes 0-31: log2-domain LSE (+inf past the end: P = 0); 32-63: Dsum
-      const int i = i0 + l32;
-      const int64_t ri = ((int64_t)b * a.Hq + h) * n + i;
-      float val = (hh == 0) ? INFINITY : 0.f;
-      if (i < n) val = (hh == 0) ? a.lse[ri] * log2e : a.dsum[ri];
-      if (hh == 0)
-        s_lse[st][l32] = val;
-      else
-        s_dsum[st][l32] = val;
-    }
+    if (wave == 0 && lane < 16)
+      dma16(uniform_rsrc(a.rowv + 2 * (((int64_t)b * a.Hq + h) * n + i0), min(rows, 32) * 8), ldst, lane * 16);
   };
 
   // row-wise A reads (rows l32 of a tile, logical chunk 2c + hh)
@@ -258,143 +269,181 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int jkey = key0 + l32;                     // this lane's key
 
-  // tiles: for each head, query tiles from the workgroup's first key on
-  const int t0 = keyw / 32;
-  const int nt = (n + 31) / 32 - t0;               // >= 1 (keyw < n)
-  const int total = a.r * nt;
-  load_tile(0, t0 * 32, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int u = 0; u <= total; ++u) {
-    if (u + 1 < total) load_tile((u + 1) / nt, (t0 + (u + 1) % nt) * 32, (u + 1) % 3);
-    // first waves: tile u; second waves: tile u - 1
+  // One step: start the DMA of tile u + kPrefetch into (dst, ldst); the first
+  // waves process tile u, the second waves tile u - 1, from (sq, sg, sl) and
+  // the P buffer pb.  The restrict-qualified pointers tell the compiler that
+  // the step's LDS reads never touch the DMA destination, so it does not
+  // hold them until the DMA lands; the waits and barrier after each step
+  // order the stages.
+  // (lhr, lti): the next tile to load; cti: the query tile index of the
+  // tile this wave processes (-1 before the second waves' first tile)
+  int lhr = __builtin_amdgcn_readfirstlane(kPrefetch / nt);
+  int lti = __builtin_amdgcn_readfirstlane(kPrefetch % nt);
+  int cti = pwave ? 0 : -1;
+  auto step = [&](int u, const unsigned char* __restrict__ sq, const unsigned char* __restrict__ sg,
+                  const float* __restrict__ sl, float* __restrict__ pb, unsigned char* __restrict__ dst,
+                  float* __restrict__ ldst) {
+    if (u + kPrefetch < total) load_tile(lhr, lti, dst, ldst);
     const int v = pwave ? u : u - 1;
-    const int i0 = (t0 + v % nt) * 32;
+    const int i0 = __builtin_amdgcn_readfirstlane((t0 + cti) * 32);
     const int i1 = min(n, i0 + 32) - 1;
-    const int st = v % 3;
-    const unsigned char* sq = &smem[st][0];
-    const unsigned char* sg = &smem[st][TILE_B];
-    float* pbuf = &s_p[v & 1][pair][0];
-    if (v >= 0 && v < total && wave_valid && i1 >= key0) {
-      const int lD = max(0, i0 - key1);
-      const int rD = i1 - key0;
-      int sL, sR;
-      split_points<NG>(a.cut, lD, rD, sL, sR);
-      auto rop = [&](const unsigned char* t, int c) { return *reinterpret_cast<const u32x4*>(t + rread[c]); };
-      if (pwave) {
-        // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
-        f32x16 s = zero16;
-        if (sR < NG) {
-          s = mfma32(rop(sq, NCH - 1), br[NCH - 1], zero16);
+    if (!(v >= 0 && v < total && wave_valid && i1 >= key0)) return;
+    const int lD = max(0, i0 - key1);
+    const int rD = i1 - key0;
+    int sL, sR;
+    split_points<NG>(a.cut, lD, rD, sL, sR);
+    auto rop = [&](const unsigned char* t, int c) { return *reinterpret_cast<const u32x4*>(t + rread[c]); };
+    if (pwave) {
+      // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
+      f32x16 s = zero16;
+      if (sR < NG) {
+        s = mfma32(rop(sq, NCH - 1), br[NCH - 1], zero16);
 #pragma unroll
-          for (int cc = NCH - 2; cc >= 0; --cc) {
-            if (cc < sR * GC) break;
-            s = mfma32(rop(sq, cc), br[cc], s);
-          }
+        for (int cc = NCH - 2; cc >= 0; --cc) {
+          if (cc < sR * GC) break;
+          s = mfma32(rop(sq, cc), br[cc], s);
         }
-        if (sL < sR) {
+      }
+      if (sL < sR) {
 #pragma unroll
-          for (int g = NG - 1; g >= 0; --g) {
-            if (g >= sR || g < sL) continue;
-            f32x16 t = zero16;
+        for (int g = NG - 1; g >= 0; --g) {
+          if (g >= sR || g < sL) continue;
+          f32x16 t = zero16;
 #pragma unroll
-            for (int c = 0; c < GC; ++c) t = mfma32(rop(sq, g * GC + c), br[g * GC + c], t);
+          for (int c = 0; c < GC; ++c) t = mfma32(rop(sq, g * GC + c), br[g * GC + c], t);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
-          }
+          for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
         }
-        // ---- P (queries before the key masked), to the partner and packed ----
-        f32x16 pm;
+      }
+      // ---- P, to the partner and packed; queries before the key or past
+      //      the end are masked, on the tiles that have such queries ----
+      f32x16 pm;
+      const bool interior = i0 >= key1 && i0 + 31 < n;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rb = 8 * r4 + 4 * hh;                // first of 4 consecutive rows
-          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[st][rb]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          float4 p4;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = 8 * r4 + 4 * hh;                  // first of 4 consecutive rows
+        const float4 x = *reinterpret_cast<const float4*>(sl + 2 * rb);
+        const float4 y = *reinterpret_cast<const float4*>(sl + 2 * rb + 4);
+        const float lv[4] = {x.x, x.z, y.x, y.z};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pm[4 * r4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * r4 + e], sl2, -lv[e]));
+        if (!interior) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            const bool keep = i0 + rb + e >= jkey;
-            pm[r] = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lv[e])) : 0.f;
+            const int i = i0 + rb + e;
+            pm[4 * r4 + e] = (i >= jkey && i < n) ? pm[4 * r4 + e] : 0.f;
           }
-          p4.x = pm[4 * r4];
-          p4.y = pm[4 * r4 + 1];
-          p4.z = pm[4 * r4 + 2];
-          p4.w = pm[4 * r4 + 3];
-          *reinterpret_cast<float4*>(pbuf + (r4 * 64 + lane) * 4) = p4;
         }
-        u32x4 pp[2];
-        pack_block(pm, pp);
-        // ---- dV^T += dO^T P ----
+        *reinterpret_cast<float4*>(pb + (r4 * 64 + lane) * 4) =
+            float4{pm[4 * r4], pm[4 * r4 + 1], pm[4 * r4 + 2], pm[4 * r4 + 3]};
+      }
+      u32x4 pp[2];
+      pack_block(pm, pp);
+      // ---- dV^T += dO^T P ----
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const u32x2 lo = read_tr16(sg + kc * 16 * RB + tlo[db]);
-            const u32x2 hi = read_tr16(sg + kc * 16 * RB + thi[db]);
-            acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pp[kc], acc[db]);
-          }
-      } else {
-        // ---- dP = dO V^T ----
-        f32x16 dp = mfma32(rop(sg, 0), br[0], zero16);
-#pragma unroll
-        for (int c = 1; c < NCH; ++c) dp = mfma32(rop(sg, c), br[c], dp);
-        // ---- dS = P (dP - Dsum), P from the partner ----
-        f32x16 ds;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rb = 8 * r4 + 4 * hh;
-          const float4 d4 = *reinterpret_cast<const float4*>(&s_dsum[st][rb]);
-          const float4 p4 = *reinterpret_cast<const float4*>(pbuf + (r4 * 64 + lane) * 4);
-          ds[4 * r4] = p4.x * (dp[4 * r4] - d4.x);
-          ds[4 * r4 + 1] = p4.y * (dp[4 * r4 + 1] - d4.y);
-          ds[4 * r4 + 2] = p4.z * (dp[4 * r4 + 2] - d4.z);
-          ds[4 * r4 + 3] = p4.w * (dp[4 * r4 + 3] - d4.w);
-        }
-        u32x4 dsp[2];
-        pack_block(ds, dsp);
-        // ---- dK^T += Q^T dS, masked per group ----
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-          const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
-          if (ga >= sR) {                                 // every group of the block full
+          const u32x2 lo = read_tr16(sg + kc * 16 * RB + tlo[db]);
+          const u32x2 hi = read_tr16(sg + kc * 16 * RB + thi[db]);
+          acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pp[kc], acc[db]);
+        }
+    } else {
+      // ---- dP = dO V^T ----
+      f32x16 dp = mfma32(rop(sg, 0), br[0], zero16);
+#pragma unroll
+      for (int c = 1; c < NCH; ++c) dp = mfma32(rop(sg, c), br[c], dp);
+      // ---- dS = P (dP - Dsum), P from the partner ----
+      f32x16 ds;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = 8 * r4 + 4 * hh;
+        const float4 x = *reinterpret_cast<const float4*>(sl + 2 * rb);
+        const float4 y = *reinterpret_cast<const float4*>(sl + 2 * rb + 4);
+        const float dv[4] = {x.y, x.w, y.y, y.w};
+        const float4 p4 = *reinterpret_cast<const float4*>(pb + (r4 * 64 + lane) * 4);
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = pv[e] * (dp[4 * r4 + e] - dv[e]);
+      }
+      u32x4 dsp[2];
+      pack_block(ds, dsp);
+      // ---- dK^T += Q^T dS, masked per group ----
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
+        if (ga >= sR) {                                 // every group of the block full
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
+            const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
+            acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], acc[db]);
+          }
+        } else {
+#pragma unroll
+          for (int g = ga; g <= gb; ++g) {
+            if (g < sL) continue;                         // skipped: no contribution
+            u32x4 bop[2];
+            if (g >= sR) {
+              bop[0] = dsp[0];
+              bop[1] = dsp[1];
+            } else {
+              f32x16 dm;
+              const int cg = a.cut[g];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
+              pack_block(dm, bop);
+            }
+            const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
               const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
               const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-              acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], acc[db]);
-            }
-          } else {
-#pragma unroll
-            for (int g = ga; g <= gb; ++g) {
-              if (g < sL) continue;                         // skipped: no contribution
-              u32x4 bop[2];
-              if (g >= sR) {
-                bop[0] = dsp[0];
-                bop[1] = dsp[1];
-              } else {
-                f32x16 dm;
-                const int cg = a.cut[g];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
-                pack_block(dm, bop);
-              }
-              const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
-#pragma unroll
-              for (int kc = 0; kc < 2; ++kc) {
-                const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
-                const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-                const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
-                acc[db] = mfma32(aop, bop[kc], acc[db]);
-              }
+              const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
+              acc[db] = mfma32(aop, bop[kc], acc[db]);
             }
           }
         }
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  };
+
+  // The resident operand is complete before the loop (an empty asm use
+  // makes the compiler wait for it here, not inside it).
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) asm volatile("" ::"v"(br[c]));
+  // tiles 0 .. kPrefetch-1 into stages 0 .. kPrefetch-1
+#pragma unroll
+  for (int t = 0; t < kPrefetch; ++t)
+    if (t < total) load_tile(t / nt, t % nt, &smem[t][0], &s_ld[t][0]);
+  wait_vm<0>();
+  bare_barrier();
+
+  for (int u = 0; u <= total; ++u) {
+    // first waves: tile u; second waves: tile u - 1 (tile t sits in stage
+    // t % kStages); the DMA fills the stage of tile u + kPrefetch, last read
+    // in step u - 1
+    const int v = pwave ? u : u - 1;
+    const int st = (v + kStages) % kStages;
+    const int nx = (u + kPrefetch) % kStages;
+    step(u, &smem[st][0], &smem[st][TILE_B], &s_ld[st][0], &s_p[(v + 2) & 1][pair][0], &smem[nx][0], &s_ld[nx][0]);
+    if (++lti == nt) {
+      lti = 0;
+      ++lhr;
+    }
+    if (++cti == nt) cti = 0;
+    // tile u + 1 must have landed (later tiles may still be in flight)
+    // and every wave be done with this step's stages
+    const int ahead = min(total - 1, u + kPrefetch) - (u + 1);   // tiles issued after u + 1
+    if (ahead <= 0) {
+      wait_vm<0>();
+    } else if (wave == 0) {
+      if (ahead == 1) wait_vm<NL + 1>(); else wait_vm<2 * (NL + 1)>();
+    } else {
+      if (ahead == 1) wait_vm<NL>(); else wait_vm<2 * NL>();
+    }
+    bare_barrier();
   }
 
   // ---- dV = dV^T (first waves), dK = scale * dK^T (second): lane's key,
@@ -420,8 +469,11 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
 // dQ: a wave owns 32 queries of one head (4 waves: HPW heads x 4/HPW query
 // blocks sharing one kv head); the workgroup streams 64-key K / V tiles.
 // ---------------------------------------------------------------------------
+constexpr int kDqWaves = 4;
+constexpr int kDqThreads = 64 * kDqWaves;
+
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int NCH = D / 16;
   constexpr int GC = G / 16;
   constexpr int NG = D / G;
@@ -429,9 +481,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int TILE_B = 64 * RB;
-  constexpr int LOADS = TILE_B / (kWaves * 64 * 16);
+  constexpr int LOADS = TILE_B / (kDqWaves * 64 * 16);
   constexpr int KRB = 256 / RB;
-  static_assert(LOADS >= 1 && TILE_B % (kWaves * 64 * 16) == 0, "tile shape");
+  static_assert(LOADS >= 1 && TILE_B % (kDqWaves * 64 * 16) == 0, "tile shape");
 
   // [stage][K tile | V tile]
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
@@ -441,20 +493,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int QSUB = kWaves / a.HPW;
+  const int QSUB = kDqWaves / a.HPW;
   const int QB = 32 * QSUB;
   const int nqb = (a.n + QB - 1) / QB;
 
+  // block decomposition, kept scalar (the divisions run on the vector unit)
   int bid = blockIdx.x;
-  const int kvh = bid % a.Hkv;
+  const int kvh = __builtin_amdgcn_readfirstlane(bid % a.Hkv);
   bid /= a.Hkv;
-  const int hg = bid % a.HG;
+  const int hg = __builtin_amdgcn_readfirstlane(bid % a.HG);
   bid /= a.HG;
-  const int b = bid % a.B;
+  const int b = __builtin_amdgcn_readfirstlane(bid % a.B);
   bid /= a.B;
-  const int qblk = nqb - 1 - bid;                  // heaviest first
+  const int qblk = __builtin_amdgcn_readfirstlane(nqb - 1 - bid);   // heaviest first
   const int n = a.n;
-  const int h = kvh * a.r + hg * a.HPW + (wave % a.HPW);
+  const int h = __builtin_amdgcn_readfirstlane(kvh * a.r + hg * a.HPW + (wave % a.HPW));
   const int i0_wg = qblk * QB;
   const int i0w = __builtin_amdgcn_readfirstlane(i0_wg + (wave / a.HPW) * 32);
   const bool wave_valid = i0w < n;
@@ -475,13 +528,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
       gr[c] = (qi < n) ? *reinterpret_cast<const u32x4*>(gp + c * 16) : zero;
     }
   }
-  const float log2e = 1.4426950408889634f;
-  const int64_t rq = ((int64_t)b * a.Hq + h) * n + qi;
-  float lse2 = INFINITY;                           // past the end: P = 0
+  // the lane's query row: LSE in base 2 (+inf past the end: P = 0), Dsum
+  float lse2 = INFINITY;
   float dsq = 0.f;
   if (qi < n) {
-    lse2 = a.lse[rq] * log2e;
-    dsq = a.dsum[rq];
+    const float2 rv = *reinterpret_cast<const float2*>(a.rowv + 2 * (((int64_t)b * a.Hq + h) * n + qi));
+    lse2 = rv.x;
+    dsq = rv.y;
   }
 
   const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
@@ -593,13 +646,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BackwardArgs a) {
         f32x16 dp = mfma32(vop(kb, 0), gr[0], zero16);
 #pragma unroll
         for (int c = 1; c < NCH; ++c) dp = mfma32(vop(kb, c), gr[c], dp);
-        // ---- P^T, dS^T; keys after the query are masked ----
+        // ---- P^T, dS^T; keys after the query are masked, on the key
+        //      blocks that reach past the wave's first query ----
+        f32x16 pr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool keep = base - 32 * kb - out_row(r, hh) >= 0;
-          const float pr = keep ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2)) : 0.f;
-          dsv[kb][r] = pr * (dp[r] - dsq);
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -lse2));
+        if (j0 + 32 * kb + 31 > i0w) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = (base - 32 * kb - out_row(r, hh) >= 0) ? pr[r] : 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsv[kb][r] = pr[r] * (dp[r] - dsq);
         u32x4 pk[2];
         pack_block(dsv[kb], pk);
         dsp[2 * kb] = pk[0];
@@ -680,9 +737,9 @@ hipError_t launch_bwd(const BackwardArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)kblocks), dim3(kKvThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int QB = 32 * (kWaves / a.HPW);
+  const int QB = 32 * (kDqWaves / a.HPW);
   const long long qblocks = (long long)a.Hkv * a.HG * a.B * ((a.n + QB - 1) / QB);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)qblocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, s, a);
   return hipGetLastError();
 }
 

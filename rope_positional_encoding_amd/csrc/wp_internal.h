@@ -111,7 +111,7 @@ struct BackwardArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;    // [B][Hq][n], natural log, from the forward pass
-  float* dsum;         // [B][Hq][n] workspace: rowsum(dO * O)
+  float* rowv;         // [B][Hq][n][2] workspace: (LSE * log2(e), rowsum(dO * O))
   bf16* dq;
   bf16* dk;
   bf16* dv;

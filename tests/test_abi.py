@@ -294,3 +294,36 @@ def test_status_strings():
     for s in range(0, -8, -1):
         assert L.wp_status_string(s)
     assert L.wp_version().decode().count(".") == 2
+
+
+def _backward(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, n=64,
+                Hq=4, Hkv=2, d_h=128, strides=_strides(24), cut=(ctypes.c_int32 * 8)(*range(8)), G=16,
+                flags=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return W.lib().wp_prefill_backward(*args.values())
+
+
+def test_backward_workspace_size():
+    # two floats per query row (its base-2 LSE and Dsum), rounded up to 256 bytes
+    L = W.lib()
+    assert L.wp_prefill_backward_workspace_size(2, 1000, 8) == 2 * 1000 * 8 * 8
+    assert L.wp_prefill_backward_workspace_size(1, 3, 1) == 256
+    assert L.wp_prefill_backward_workspace_size(0, 10, 1) == 0
+
+
+def test_backward_validation_codes():
+    # every call here fails validation, so no kernel is launched
+    assert _backward(lse=None) == -1
+    assert _backward(dv=None) == -1
+    assert _backward(d_h=96) == -3
+    assert _backward(Hq=3) == -2
+    assert _backward(n=0) == -2
+    assert _backward(ws_bytes=1024) == -5                # need 1 * 4 * 64 * 8 bytes
+    assert _backward(flags=2) == -6                      # only WP_FLAG_DENSE is known
+    assert _backward(cut=None) == -1
+    assert _backward(cut=(ctypes.c_int32 * 8)(9, 8, 7, 6, 5, 4, 3, 2)) == -6
+    assert _backward(ws=ctypes.c_void_p(0x7F0000000010)) == -4
+    st = _strides(24)
+    st[13] = 64                                          # dO token stride < d_h
+    assert _backward(strides=st) == -2
