@@ -115,6 +115,21 @@ __device__ inline void pack_block(const f32x16& x, u32x4 (&p)[2]) {
     for (int w = 0; w < 4; ++w) p[c][w] = pack_bf16x2(x[8 * c + 2 * w], x[8 * c + 2 * w + 1]);
 }
 
+// Zeroes the bf16 entries of a packed block (pack_block's layout) whose
+// row r fails keep(r): word p[c][w] holds rows 8c + 2w (low half) and
+// 8c + 2w + 1 (high half) of this lane's 16 values.
+template <typename F>
+__device__ inline void mask_block(u32x4 (&p)[2], F keep) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned lo = keep(8 * c + 2 * w) ? 0x0000ffffu : 0u;
+      const unsigned hi = keep(8 * c + 2 * w + 1) ? 0xffff0000u : 0u;
+      p[c][w] &= lo | hi;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dK / dV.  A workgroup owns 128 keys of one kv head and streams the 32-query
 // tiles of every query head of that kv head.  Its 8 waves work in pairs;
@@ -130,8 +145,15 @@ __device__ inline void pack_block(const f32x16& x, u32x4 (&p)[2]) {
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kPrefetch = 1;                      // tiles in flight ahead of use
+constexpr int kPrefetch = 2;                      // tiles in flight ahead of use
 constexpr int kStages = kPrefetch + 2;            // + the tiles of both halves of a pair
+
+// compile-time role of a wave in a pair (the two roles run separate loops,
+// so that each loop updates its accumulators along one code path)
+template <bool P>
+struct Role {
+  static constexpr bool first = P;
+};
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -274,17 +296,14 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   // the P buffer pb.  The restrict-qualified pointers tell the compiler that
   // the step's LDS reads never touch the DMA destination, so it does not
   // hold them until the DMA lands; the waits and barrier after each step
-  // order the stages.
-  // (lhr, lti): the next tile to load; cti: the query tile index of the
-  // tile this wave processes (-1 before the second waves' first tile)
-  int lhr = __builtin_amdgcn_readfirstlane(kPrefetch / nt);
-  int lti = __builtin_amdgcn_readfirstlane(kPrefetch % nt);
-  int cti = pwave ? 0 : -1;
-  auto step = [&](int u, const unsigned char* __restrict__ sq, const unsigned char* __restrict__ sg,
-                  const float* __restrict__ sl, float* __restrict__ pb, unsigned char* __restrict__ dst,
-                  float* __restrict__ ldst) {
+  // order the stages.  (lhr, lti): head and query tile index of the tile to
+  // load; cti: query tile index of the tile to process.
+  auto step = [&](auto role, int u, int lhr, int lti, int cti, const unsigned char* __restrict__ sq,
+                  const unsigned char* __restrict__ sg, const float* __restrict__ sl, float* __restrict__ pb,
+                  unsigned char* __restrict__ dst, float* __restrict__ ldst) {
+    constexpr bool PW = decltype(role)::first;
     if (u + kPrefetch < total) load_tile(lhr, lti, dst, ldst);
-    const int v = pwave ? u : u - 1;
+    const int v = PW ? u : u - 1;
     const int i0 = __builtin_amdgcn_readfirstlane((t0 + cti) * 32);
     const int i1 = min(n, i0 + 32) - 1;
     if (!(v >= 0 && v < total && wave_valid && i1 >= key0)) return;
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     int sL, sR;
     split_points<NG>(a.cut, lD, rD, sL, sR);
     auto rop = [&](const unsigned char* t, int c) { return *reinterpret_cast<const u32x4*>(t + rread[c]); };
-    if (pwave) {
+    if constexpr (PW) {
       // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
       f32x16 s = zero16;
       if (sR < NG) {
@@ -369,42 +388,45 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
       }
       u32x4 dsp[2];
       pack_block(ds, dsp);
-      // ---- dK^T += Q^T dS, masked per group ----
+      // ---- dK^T += Q^T dS, masked per group.  Each update is a uniform
+      //      "if" around in-place MFMAs, so the accumulators stay put. ----
+      // full groups [sR, NG): unmasked dS; A rows (dims) of other groups zero
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
         const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
-        if (ga >= sR) {                                 // every group of the block full
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
-            const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-            acc[db] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, dsp[kc], acc[db]);
-          }
-        } else {
-#pragma unroll
-          for (int g = ga; g <= gb; ++g) {
-            if (g < sL) continue;                         // skipped: no contribution
-            u32x4 bop[2];
-            if (g >= sR) {
-              bop[0] = dsp[0];
-              bop[1] = dsp[1];
-            } else {
-              f32x16 dm;
-              const int cg = a.cut[g];
-#pragma unroll
-              for (int r = 0; r < 16; ++r) dm[r] = (i0 + out_row(r, hh) - jkey <= cg) ? ds[r] : 0.f;
-              pack_block(dm, bop);
-            }
-            const bool mine = ((32 * db + l32) / G) == g;   // A row (dim) in group g
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-              const u32x2 lo = read_tr16(sq + kc * 16 * RB + tlo[db]);
-              const u32x2 hi = read_tr16(sq + kc * 16 * RB + thi[db]);
-              const u32x4 aop = mine ? u32x4{lo[0], lo[1], hi[0], hi[1]} : zero4;
-              acc[db] = mfma32(aop, bop[kc], acc[db]);
-            }
-          }
+        if (gb < sR) continue;                            // no full group in the block
+        const u32x2 lo0 = read_tr16(sq + tlo[db]);
+        const u32x2 hi0 = read_tr16(sq + thi[db]);
+        const u32x2 lo1 = read_tr16(sq + 16 * RB + tlo[db]);
+        const u32x2 hi1 = read_tr16(sq + 16 * RB + thi[db]);
+        u32x4 a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+        u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+        if (ga < sR) {
+          const bool keep = (32 * db + l32) / G >= sR;
+          a0 = keep ? a0 : zero4;
+          a1 = keep ? a1 : zero4;
         }
+        acc[db] = mfma32(a0, dsp[0], acc[db]);
+        acc[db] = mfma32(a1, dsp[1], acc[db]);
+      }
+      // partial groups [sL, sR): dS masked by the group's cutoff, A rows of
+      // the group only
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g < sL || g >= sR) continue;
+        const int db = (g * G) / 32;
+        u32x4 bop[2] = {dsp[0], dsp[1]};
+        const int cg = a.cut[g];
+        mask_block(bop, [&](int r) { return i0 + out_row(r, hh) - jkey <= cg; });
+        const bool mine = ((32 * db + l32) / G) == g;
+        const u32x2 lo0 = read_tr16(sq + tlo[db]);
+        const u32x2 hi0 = read_tr16(sq + thi[db]);
+        const u32x2 lo1 = read_tr16(sq + 16 * RB + tlo[db]);
+        const u32x2 hi1 = read_tr16(sq + 16 * RB + thi[db]);
+        const u32x4 a0 = mine ? u32x4{lo0[0], lo0[1], hi0[0], hi0[1]} : zero4;
+        const u32x4 a1 = mine ? u32x4{lo1[0], lo1[1], hi1[0], hi1[1]} : zero4;
+        acc[db] = mfma32(a0, bop[0], acc[db]);
+        acc[db] = mfma32(a1, bop[1], acc[db]);
       }
     }
   };
@@ -420,31 +442,44 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   wait_vm<0>();
   bare_barrier();
 
-  for (int u = 0; u <= total; ++u) {
-    // first waves: tile u; second waves: tile u - 1 (tile t sits in stage
-    // t % kStages); the DMA fills the stage of tile u + kPrefetch, last read
-    // in step u - 1
-    const int v = pwave ? u : u - 1;
-    const int st = (v + kStages) % kStages;
-    const int nx = (u + kPrefetch) % kStages;
-    step(u, &smem[st][0], &smem[st][TILE_B], &s_ld[st][0], &s_p[(v + 2) & 1][pair][0], &smem[nx][0], &s_ld[nx][0]);
-    if (++lti == nt) {
-      lti = 0;
-      ++lhr;
+  auto run = [&](auto role) {
+    constexpr bool PW = decltype(role)::first;
+    // (lhr, lti): the next tile to load; cti: the query tile index of the
+    // tile this wave processes (-1 before the second waves' first tile)
+    int lhr = __builtin_amdgcn_readfirstlane(kPrefetch / nt);
+    int lti = __builtin_amdgcn_readfirstlane(kPrefetch % nt);
+    int cti = PW ? 0 : -1;
+    for (int u = 0; u <= total; ++u) {
+      // first waves: tile u; second waves: tile u - 1 (tile t sits in stage
+      // t % kStages); the DMA fills the stage of tile u + kPrefetch, last
+      // read in step u - 1
+      const int v = PW ? u : u - 1;
+      const int st = (v + kStages) % kStages;
+      const int nx = (u + kPrefetch) % kStages;
+      step(role, u, lhr, lti, cti, &smem[st][0], &smem[st][TILE_B], &s_ld[st][0], &s_p[(v + 2) & 1][pair][0],
+           &smem[nx][0], &s_ld[nx][0]);
+      if (++lti == nt) {
+        lti = 0;
+        ++lhr;
+      }
+      if (++cti == nt) cti = 0;
+      // tile u + 1 must have landed (later tiles may still be in flight)
+      // and every wave be done with this step's stages
+      const int ahead = min(total - 1, u + kPrefetch) - (u + 1);   // tiles issued after u + 1
+      if (ahead <= 0) {
+        wait_vm<0>();
+      } else if (wave == 0) {
+        if (ahead == 1) wait_vm<NL + 1>(); else wait_vm<2 * (NL + 1)>();
+      } else {
+        if (ahead == 1) wait_vm<NL>(); else wait_vm<2 * NL>();
+      }
+      bare_barrier();
     }
-    if (++cti == nt) cti = 0;
-    // tile u + 1 must have landed (later tiles may still be in flight)
-    // and every wave be done with this step's stages
-    const int ahead = min(total - 1, u + kPrefetch) - (u + 1);   // tiles issued after u + 1
-    if (ahead <= 0) {
-      wait_vm<0>();
-    } else if (wave == 0) {
-      if (ahead == 1) wait_vm<NL + 1>(); else wait_vm<2 * (NL + 1)>();
-    } else {
-      if (ahead == 1) wait_vm<NL>(); else wait_vm<2 * NL>();
-    }
-    bare_barrier();
-  }
+  };
+  if (pwave)
+    run(Role<true>{});
+  else
+    run(Role<false>{});
 
   // ---- dV = dV^T (first waves), dK = scale * dK^T (second): lane's key,
   // rows = dims ----
