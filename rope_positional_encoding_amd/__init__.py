@@ -106,6 +106,13 @@ def _i32arr(vals: Sequence[int]):
     return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
 
 
+def _cut(cutoffs: Sequence[int], d_h: int, G: int):
+    """The group cutoff table as a C array; the library reads d_h / G entries."""
+    if G > 0 and d_h % G == 0 and len(cutoffs) != d_h // G:
+        raise ValueError("expected %d cutoffs (d_h / G), got %d" % (d_h // G, len(cutoffs)))
+    return _i32arr(cutoffs)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -170,14 +177,14 @@ def decode_tiling(d_h: int, G: int) -> int:
 def prefill_tile_counts(n: int, d_h: int, G: int, cutoffs: Sequence[int]):
     ng = d_h // G
     out = (ctypes.c_int64 * (3 * ng + 1))()
-    _check(lib().wp_prefill_tile_counts(n, d_h, G, _i32arr(cutoffs), out))
+    _check(lib().wp_prefill_tile_counts(n, d_h, G, _cut(cutoffs, d_h, G), out))
     return [int(v) for v in out]
 
 
 def decode_tile_counts(q_pos: int, cache_len: int, d_h: int, G: int, cutoffs: Sequence[int]):
     ng = d_h // G
     out = (ctypes.c_int64 * (3 * ng + 1))()
-    _check(lib().wp_decode_tile_counts(q_pos, cache_len, d_h, G, _i32arr(cutoffs), out))
+    _check(lib().wp_decode_tile_counts(q_pos, cache_len, d_h, G, _cut(cutoffs, d_h, G), out))
     return [int(v) for v in out]
 
 
@@ -232,7 +239,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cutoffs: Optional
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
     flags = (FLAG_DENSE if dense else 0) | (FLAG_COUNT if counters is not None else 0)
-    cut = None if cutoffs is None else _i32arr(cutoffs)
+    cut = None if cutoffs is None else _cut(cutoffs, d, G)
     strides = list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3]) + list(out.stride()[:3])
     _check(lib().wp_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, n, Hq, Hkv, d, _i64arr(strides), cut,
@@ -264,7 +271,7 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     strides = []
     for t in (q, k, v, o, dout, dq, dk, dv):
         strides += list(t.stride()[:3])
-    cut = None if cutoffs is None else _i32arr(cutoffs)
+    cut = None if cutoffs is None else _cut(cutoffs, d, G)
     _check(lib().wp_prefill_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
         B, n, Hq, Hkv, d, _i64arr(strides), cut, int(G), FLAG_DENSE if dense else 0, _ptr(workspace),
@@ -295,7 +302,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
     flags = (FLAG_DENSE if dense else 0) | (FLAG_COUNT if counters is not None else 0)
-    cut = None if cutoffs is None else _i32arr(cutoffs)
+    cut = None if cutoffs is None else _cut(cutoffs, d, G)
     strides = (list(q.stride()[:2]) + list(k_cache.stride()[:3]) + list(v_cache.stride()[:3])
                + list(out.stride()[:2]))
     _check(lib().wp_decode(
@@ -311,7 +318,7 @@ def kcache_layout(Lmax: int, d_h: int, G: int, cutoffs: Sequence[int]):
     ng = d_h // G
     caps = (ctypes.c_int32 * max(ng, 1))()
     offs = (ctypes.c_int64 * (ng + 1))()
-    _check(lib().wp_kcache_layout(int(Lmax), int(d_h), int(G), _i32arr(cutoffs), caps, offs))
+    _check(lib().wp_kcache_layout(int(Lmax), int(d_h), int(G), _cut(cutoffs, d_h, G), caps, offs))
     return [int(v) for v in caps[:ng]], [int(v) for v in offs]
 
 
@@ -334,7 +341,7 @@ def kcache_append(k: torch.Tensor, pos0: torch.Tensor, store: torch.Tensor, Lmax
         raise ValueError("store must be [B, Hkv, elements] (elements contiguous) matching k")
     _check(lib().wp_kcache_append(
         _ptr(k), B, T, Hkv, d, _i64arr(list(k.stride()[:3])), _ptr(pos0), _ptr(store),
-        _i64arr(list(store.stride()[:2])), int(Lmax), _i32arr(cutoffs), int(G), _stream(k)))
+        _i64arr(list(store.stride()[:2])), int(Lmax), _cut(cutoffs, d, G), int(G), _stream(k)))
     return store
 
 
@@ -366,6 +373,6 @@ def decode_kcache(q: torch.Tensor, store: torch.Tensor, v_cache: torch.Tensor,
                + list(out.stride()[:2]))
     _check(lib().wp_decode_kcache(
         _ptr(q), _ptr(store), _ptr(v_cache), _ptr(out), _ptr(cache_len), _ptr(q_pos), B, Lmax, Hq,
-        Hkv, d, _i64arr(strides), _i32arr(cutoffs), int(G), int(num_splits), _ptr(workspace),
+        Hkv, d, _i64arr(strides), _cut(cutoffs, d, G), int(G), int(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), flags, _ptr(counters), _stream(q)))
     return out

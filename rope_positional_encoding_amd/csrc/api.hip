@@ -29,7 +29,14 @@ wp_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Prefill and decode: groups of 16 or 32 dims (one or two MFMA steps per
+// group) and the fine groups 2, 4, 8 (G = 2 is one cutoff per channel, the
+// exact rule).  The backward pass and the compact K store take 16 or 32.
 bool supported_shape(int32_t d_h, int32_t G) {
+  return (d_h == 64 || d_h == 128) && (G == 2 || G == 4 || G == 8 || G == 16 || G == 32);
+}
+
+bool supported_coarse(int32_t d_h, int32_t G) {
   return (d_h == 64 || d_h == 128) && (G == 16 || G == 32);
 }
 
@@ -376,6 +383,8 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
   if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
   if (count && !counters) return fail(WP_ERR_NULL, "counters is NULL with WP_FLAG_COUNT");
   if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (compact && !supported_coarse(d_h, G))
+    return fail(WP_ERR_UNSUPPORTED, "the compact K store takes G = 16 or 32 (G=%d)", G);
   if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, Lmax, Hq, Hkv must be >= 1");
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(WP_ERR_UNSUPPORTED, "decode supports at most 16 query heads per kv head");
@@ -408,7 +417,7 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
   }
   if (compact) {
     if (Lmax > (1 << 24)) return fail(WP_ERR_SHAPE, "the compact K store supports Lmax <= 2^24");
-    int64_t off[wp::kMaxGroups + 1];
+    int64_t off[wp::kMaxCacheGroups + 1];
     kcache_geometry(Lmax, ng, G, cutoffs, a.kcap, off);
     if (st10[2] < off[ng] || st10[4] < off[ng])
       return fail(WP_ERR_SHAPE, "K store strides must be >= the store size (%lld elements)", (long long)off[ng]);
@@ -471,7 +480,7 @@ wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const
   if (flags & ~WP_FLAG_DENSE) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
   const bool dense = flags & WP_FLAG_DENSE;
   if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
-  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (!supported_coarse(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
   if (B < 1 || n < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, n, Hq, Hkv must be >= 1");
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
@@ -534,12 +543,12 @@ wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const
 wp_status wp_kcache_layout(int32_t Lmax, int32_t d_h, int32_t G, const int32_t* cutoffs, int32_t* caps,
                            int64_t* offsets) {
   if (!cutoffs || !caps || !offsets) return fail(WP_ERR_NULL, "cutoffs/caps/offsets is NULL");
-  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (!supported_coarse(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
   if (Lmax < 1) return fail(WP_ERR_SHAPE, "Lmax must be >= 1");
   const int ng = d_h / G;
   if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
-  int cap[wp::kMaxGroups];
-  int64_t off[wp::kMaxGroups + 1];
+  int cap[wp::kMaxCacheGroups];
+  int64_t off[wp::kMaxCacheGroups + 1];
   kcache_geometry(Lmax, ng, G, cutoffs, cap, off);
   for (int g = 0; g < ng; ++g) caps[g] = cap[g];
   for (int g = 0; g <= ng; ++g) offsets[g] = off[g];
@@ -552,7 +561,7 @@ wp_status wp_kcache_append(const void* k, int32_t B, int32_t T, int32_t Hkv, int
                            void* stream) {
   if (!k || !k_strides || !pos0 || !store || !store_strides || !cutoffs)
     return fail(WP_ERR_NULL, "a required pointer is NULL");
-  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (!supported_coarse(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
   if (B < 1 || T < 1 || Hkv < 1 || Lmax < 1) return fail(WP_ERR_SHAPE, "B, T, Hkv, Lmax must be >= 1");
   if (T > Lmax) return fail(WP_ERR_SHAPE, "T = %d exceeds Lmax = %d", T, Lmax);
   if (Lmax > (1 << 24)) return fail(WP_ERR_SHAPE, "the compact K store supports Lmax <= 2^24");
@@ -564,7 +573,7 @@ wp_status wp_kcache_append(const void* k, int32_t B, int32_t T, int32_t Hkv, int
   if (wp_status s = check_cutoffs(cutoffs, ng)) return s;
   wp::KAppendArgs a;
   memset(&a, 0, sizeof(a));
-  int64_t off[wp::kMaxGroups + 1];
+  int64_t off[wp::kMaxCacheGroups + 1];
   kcache_geometry(Lmax, ng, G, cutoffs, a.kcap, off);
   if (store_strides[0] < off[ng] || store_strides[1] < off[ng])
     return fail(WP_ERR_SHAPE, "store strides must be >= the store size (%lld elements)", (long long)off[ng]);

@@ -59,6 +59,8 @@ template <int D, int G, bool COUNT, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int NP = D / 32;          // 32-dim MFMA steps of QK
   constexpr int NG = D / G;           // groups
+  constexpr bool FINE = G < 16;       // a lane's 8 dims may span several groups (G = 2: channels)
+  static_assert(!(FINE && COMPACT), "the compact K store takes groups of 16 or 32 dims");
   constexpr int ND = D / 16;          // 16-dim output blocks
   constexpr int VS = 32 + 8;          // V^T row stride in LDS (elements)
   constexpr int VITEMS = 8 * (D / 8) / 64;   // (key quad, chunk) items per lane
@@ -130,11 +132,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  unsigned int cnt[NG][3];
+  // Tile-class counters: per group in registers for coarse groups; for fine
+  // groups (up to 64) a workgroup histogram of splitL / splitR in LDS,
+  // turned into per-group counts at the end.
+  constexpr int CNG = FINE ? 1 : NG;
+  unsigned int cnt[CNG][3];
   unsigned int cnt_vis = 0;
+  __shared__ unsigned int s_hist[(COUNT && FINE) ? 2 * (NG + 1) : 1];
   if (COUNT) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
+    for (int g = 0; g < CNG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
+    if constexpr (FINE) {
+      if (tid < 2 * (NG + 1)) s_hist[tid] = 0;
+      __syncthreads();
+    }
   }
   const float sl2 = a.scale_log2;
 
@@ -171,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int dim = 32 * p + 8 * q4;
-        const int g = dim / G;                    // this lane's group in step p
+        const int g = (dim + 7) / G;              // the last group of this lane's 8 dims
         int off;
         if (COMPACT) {
           const int slot = mod_small(j, kcap_p[p], rcap_p[p]);
@@ -198,11 +209,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int jb1 = min(L, jb + 32) - 1;
     if (COUNT) {
       ++cnt_vis;
+      if constexpr (FINE) {
+        if (lane == 0) {
+          atomicAdd(&s_hist[sL], 1u);
+          atomicAdd(&s_hist[NG + 1 + sR], 1u);
+        }
+      } else {
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        cnt[g][0] += (g < sL);
-        cnt[g][1] += (g >= sL && g < sR);
-        cnt[g][2] += (g >= sR);
+        for (int g = 0; g < NG; ++g) {
+          cnt[g][0] += (g < sL);
+          cnt[g][1] += (g >= sL && g < sR);
+          cnt[g][2] += (g >= sR);
+        }
       }
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -218,6 +236,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         const int g_hi = (32 * p + 31) / G;
         if (g_hi < sL) continue;                   // every lane skipped
         const int g = (32 * p + 8 * q4) / G;
+        // group of operand word w (dims 32p + 8q4 + 2w, +1)
+        auto grp = [&](int w) { return (32 * p + 8 * q4 + 2 * w) / G; };
         if (g_lo >= sR) {                          // all full: skipped lanes read zero
           s[blk] = mfma16(R.k[blk][p], qr[p], s[blk]);
           continue;
@@ -226,13 +246,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int gg = g_lo; gg <= g_hi; ++gg) any_full |= (gg >= sR);
         if (any_full) {
-          const u32x4 op = (g >= sR) ? R.k[blk][p] : zero;
+          const u32x4 op = FINE ? keep_words(R.k[blk][p], [&](int w) { return grp(w) >= sR; })
+                                : ((g >= sR) ? R.k[blk][p] : zero);
           s[blk] = mfma16(op, qr[p], s[blk]);
         }
 #pragma unroll
         for (int gg = g_lo; gg <= g_hi; ++gg) {
           if (gg < sL || gg >= sR) continue;       // only partial groups
-          const u32x4 op = (g == gg) ? R.k[blk][p] : zero;
+          const u32x4 op = FINE ? keep_words(R.k[blk][p], [&](int w) { return grp(w) == gg; })
+                                : ((g == gg) ? R.k[blk][p] : zero);
           const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
           const int cg = a.cut[gg];
 #pragma unroll
@@ -371,13 +393,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  if (COUNT && lane == 0) {
+  if (COUNT && !FINE && lane == 0) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < CNG; ++g)
 #pragma unroll
       for (int c = 0; c < 3; ++c)
         if (cnt[g][c]) atomicAdd(&a.counters[3 * g + c], (unsigned long long)cnt[g][c]);
     if (cnt_vis) atomicAdd(&a.counters[3 * NG], (unsigned long long)cnt_vis);
+  }
+  if constexpr (COUNT && FINE) {
+    // every block was counted before the merge barriers; thread g turns the
+    // split histograms into group g's counts
+    if (tid < NG) {
+      unsigned int skip = 0, full = 0, vis = 0;
+      for (int v = 0; v <= NG; ++v) {
+        const unsigned int hl = s_hist[v], hr = s_hist[NG + 1 + v];
+        vis += hl;
+        skip += (v > tid) ? hl : 0u;
+        full += (v <= tid) ? hr : 0u;
+      }
+      if (skip) atomicAdd(&a.counters[3 * tid], (unsigned long long)skip);
+      if (vis - skip - full) atomicAdd(&a.counters[3 * tid + 1], (unsigned long long)(vis - skip - full));
+      if (full) atomicAdd(&a.counters[3 * tid + 2], (unsigned long long)full);
+      if (tid == 0 && vis) atomicAdd(&a.counters[3 * NG], (unsigned long long)vis);
+    }
   }
 }
 
@@ -466,6 +505,14 @@ hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStr
   if (d_h == 128 && G == 32) return launch_dgc<128, 32>(a, count, s);
   if (d_h == 64 && G == 16) return launch_dgc<64, 16>(a, count, s);
   if (d_h == 64 && G == 32) return launch_dgc<64, 32>(a, count, s);
+  // fine groups: the full K cache only
+  if (a.compact) return hipErrorInvalidValue;
+  if (d_h == 128 && G == 8) return launch_dg<128, 8, false>(a, count, s);
+  if (d_h == 128 && G == 4) return launch_dg<128, 4, false>(a, count, s);
+  if (d_h == 128 && G == 2) return launch_dg<128, 2, false>(a, count, s);
+  if (d_h == 64 && G == 8) return launch_dg<64, 8, false>(a, count, s);
+  if (d_h == 64 && G == 4) return launch_dg<64, 4, false>(a, count, s);
+  if (d_h == 64 && G == 2) return launch_dg<64, 2, false>(a, count, s);
   return hipErrorInvalidValue;
 }
 

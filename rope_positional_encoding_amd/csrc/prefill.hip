@@ -61,7 +61,8 @@ constexpr int kTileKeys = 64;     // keys per tile: two 32-key MFMA blocks, one 
 template <int D, int G, bool COUNT>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int NCH = D / 16;         // 16-dim MFMA steps
-  constexpr int GC = G / 16;          // MFMA steps per group
+  constexpr bool FINE = G < 16;       // several groups per MFMA step (G = 2: one per channel)
+  constexpr int GC = FINE ? 1 : G / 16;   // MFMA steps per group (coarse groups)
   constexpr int NG = D / G;           // groups
   constexpr int ND = D / 32;          // 32-dim output blocks
   constexpr int RB = D * 2;           // bytes per K/V row in LDS (no padding)
@@ -175,11 +176,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  unsigned int cnt[NG][3];
+  // Tile-class counters.  Coarse groups: per-group counts in registers.
+  // Fine groups (up to 64): a workgroup histogram of splitL and splitR in
+  // LDS, turned into per-group counts at the end (group g is skipped on a
+  // tile with splitL > g and full on one with splitR <= g).
+  constexpr int CNG = FINE ? 1 : NG;
+  unsigned int cnt[CNG][3];
   unsigned int cnt_vis = 0;
+  __shared__ unsigned int s_hist[(COUNT && FINE) ? 2 * (NG + 1) : 1];
   if (COUNT) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
+    for (int g = 0; g < CNG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
+    if (FINE && tid < 2 * (NG + 1)) s_hist[tid] = 0;
   }
 
   const float sl2 = a.scale_log2;
@@ -211,11 +219,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       sR = __builtin_amdgcn_readfirstlane(sR);
       if (COUNT) {
         ++cnt_vis;
+        if constexpr (FINE) {
+          if (lane == 0) {
+            atomicAdd(&s_hist[sL], 1u);
+            atomicAdd(&s_hist[NG + 1 + sR], 1u);
+          }
+        } else {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          cnt[g][0] += (g < sL);
-          cnt[g][1] += (g >= sL && g < sR);
-          cnt[g][2] += (g >= sR);
+          for (int g = 0; g < NG; ++g) {
+            cnt[g][0] += (g < sL);
+            cnt[g][1] += (g >= sL && g < sR);
+            cnt[g][2] += (g >= sR);
+          }
         }
       }
 
@@ -229,8 +244,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       //      c-1 are read right after the MFMAs of step c are issued, so the
       //      LDS latency overlaps their execution. ----
       f32x16 s0 = zero16, s1 = zero16;
-      if (sR < NG) {
-        const int c_end = sR * GC;
+      // first MFMA step whose groups are all full
+      const int c_end = FINE ? (sR * G + 15) / 16 : sR * GC;
+      if (c_end < NCH) {
         const unsigned skb = lds_addr(sk);
         u32x4 ka0, ka1;
         k_reads<32 * RB>(ka0, ka1, skb + kread[NCH - 1]);
@@ -244,8 +260,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
       }
 
-      // ---- partial groups [sL, sR): compute, mask dist <= cutoff, add ----
-      if (sL < sR) {
+      if constexpr (FINE) {
+        // ---- steps [sL*G/16, c_end) mix classes: their full groups join S
+        //      with the other words of the operand zeroed, each partial
+        //      group gets its own masked MFMA ----
+        const int c_lo = (sL * G) / 16;
+        if (c_lo < c_end) {
+          const int base = (i0w + l32) - j0;     // dist = base - (32kb + out_row(r))
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            if (c < c_lo || c >= c_end) continue;
+            const u32x4 k0 = kop(0, c), k1 = kop(1, c);
+            // group of operand word w (head dims 16c + 8hh + 2w, +1)
+            auto grp = [&](int w) { return (16 * c + 8 * hh + 2 * w) / G; };
+            if ((16 * c + 15) / G >= sR) {
+              s0 = mfma32(keep_words(k0, [&](int w) { return grp(w) >= sR; }), qr[c], s0);
+              s1 = mfma32(keep_words(k1, [&](int w) { return grp(w) >= sR; }), qr[c], s1);
+            }
+#pragma unroll
+            for (int gi = 0; gi < 16 / G; ++gi) {
+              const int g = (16 * c) / G + gi;
+              if (g < sL || g >= sR) continue;
+              const int cg = a.cut[g];
+              f32x16 t = mfma32(keep_words(k0, [&](int w) { return grp(w) == g; }), qr[c], zero16);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s0[r] += (base - out_row(r, hh) <= cg) ? t[r] : 0.f;
+              t = mfma32(keep_words(k1, [&](int w) { return grp(w) == g; }), qr[c], zero16);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s1[r] += (base - 32 - out_row(r, hh) <= cg) ? t[r] : 0.f;
+            }
+          }
+        }
+      } else if (sL < sR) {
+        // ---- partial groups [sL, sR): compute, mask dist <= cutoff, add ----
         const int base = (i0w + l32) - j0;     // dist = base - (32kb + out_row(r))
 #pragma unroll
         for (int g = NG - 1; g >= 0; --g) {
@@ -344,13 +391,30 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       if (a.lse && hh == 0)
         a.lse[((int64_t)b * a.Hq + h) * n + i] = (m_i + __log2f(l_tot)) * 0.69314718055994531f;
     }
-    if (COUNT && lane == 0) {
+    if (COUNT && !FINE && lane == 0) {
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < CNG; ++g)
 #pragma unroll
         for (int c = 0; c < 3; ++c)
           if (cnt[g][c]) atomicAdd(&a.counters[3 * g + c], (unsigned long long)cnt[g][c]);
       if (cnt_vis) atomicAdd(&a.counters[3 * NG], (unsigned long long)cnt_vis);
+    }
+  }
+  if constexpr (COUNT && FINE) {
+    // every tile was counted before the last barrier of the loop; thread g
+    // turns the split histograms into group g's counts
+    if (tid < NG) {
+      unsigned int skip = 0, full = 0, vis = 0;
+      for (int v = 0; v <= NG; ++v) {
+        const unsigned int hl = s_hist[v], hr = s_hist[NG + 1 + v];
+        vis += hl;
+        skip += (v > tid) ? hl : 0u;
+        full += (v <= tid) ? hr : 0u;
+      }
+      if (skip) atomicAdd(&a.counters[3 * tid], (unsigned long long)skip);
+      if (vis - skip - full) atomicAdd(&a.counters[3 * tid + 1], (unsigned long long)(vis - skip - full));
+      if (full) atomicAdd(&a.counters[3 * tid + 2], (unsigned long long)full);
+      if (tid == 0 && vis) atomicAdd(&a.counters[3 * NG], (unsigned long long)vis);
     }
   }
 }
@@ -378,6 +442,12 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipS
   if (d_h == 128 && G == 32) return launch_dg<128, 32>(a, count, s);
   if (d_h == 64 && G == 16) return launch_dg<64, 16>(a, count, s);
   if (d_h == 64 && G == 32) return launch_dg<64, 32>(a, count, s);
+  if (d_h == 128 && G == 8) return launch_dg<128, 8>(a, count, s);
+  if (d_h == 128 && G == 4) return launch_dg<128, 4>(a, count, s);
+  if (d_h == 128 && G == 2) return launch_dg<128, 2>(a, count, s);
+  if (d_h == 64 && G == 8) return launch_dg<64, 8>(a, count, s);
+  if (d_h == 64 && G == 4) return launch_dg<64, 4>(a, count, s);
+  if (d_h == 64 && G == 2) return launch_dg<64, 2>(a, count, s);
   return hipErrorInvalidValue;
 }
 

@@ -81,6 +81,16 @@ __device__ inline float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A 16-byte MFMA operand with the 4-byte words (dim pairs) for which
+// keep(w) fails set to zero.
+template <typename F>
+__device__ inline u32x4 keep_words(const u32x4& x, F keep) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r[w] = keep(w) ? x[w] : 0u;
+  return r;
+}
+
 // Row (key) of register r of a 32x32 MFMA output block for lane half hh.
 __device__ inline int out_row(int r, int hh) { return ((r >> 2) << 3) + (hh << 2) + (r & 3); }
 

@@ -14,7 +14,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxGroups = 8;       // d_h / G for d_h <= 128, G >= 16
+constexpr int kMaxGroups = 64;      // d_h / G for d_h <= 128, G >= 2 (G = 2: one group per channel)
+constexpr int kMaxCacheGroups = 8;  // groups of the compact K store (G >= 16)
 constexpr int kMaxChannels = 64;    // d_h / 2 for d_h <= 128
 
 // Tile geometry shared by the kernels, the host classifier and the tiling
@@ -85,8 +86,8 @@ struct DecodeArgs {
   // j % kcap[g], so consecutive keys of a group are contiguous.
   int compact;
   int kstore_elems;   // elements of one (sequence, kv head) store
-  int kcap[kMaxGroups];
-  int koff[kMaxGroups];
+  int kcap[kMaxCacheGroups];
+  int koff[kMaxCacheGroups];
 };
 
 // Appending keys to the compact K store: token t of row b (position
@@ -99,8 +100,8 @@ struct KAppendArgs {
   int64_t ks_b, ks_t, ks_h;
   int64_t ss_b, ss_h;
   int B, T, Hkv, d_h, G, ng;
-  int kcap[kMaxGroups];
-  int koff[kMaxGroups];
+  int kcap[kMaxCacheGroups];
+  int koff[kMaxCacheGroups];
 };
 
 // Backward pass of prefill (gradients of <dO, O>).

@@ -183,7 +183,8 @@ def test_tiling_queries():
 
 @pytest.mark.parametrize("n", [1, 31, 32, 33, 256, 1000, 4096])
 @pytest.mark.parametrize("cfg", [(64, 16, 1e4, 1.0), (128, 16, 1e6, 1.0), (128, 32, 1e6, 1.0),
-                                 (128, 16, 1e6, 4.0), (64, 32, 100.0, 1.0), (128, 16, 30.0, 1.0)])
+                                 (128, 16, 1e6, 4.0), (64, 32, 100.0, 1.0), (128, 16, 30.0, 1.0),
+                                 (128, 2, 1e4, 1.0), (128, 4, 1e6, 1.0), (64, 8, 300.0, 1.0)])
 def test_host_prefill_classifier_matches_oracle(n, cfg):
     d_h, G, theta, s = cfg
     cut = [int(v) for v in O.group_cutoffs(theta, d_h, G, s)]
@@ -204,7 +205,7 @@ def test_host_prefill_classifier_32k_and_128k():
 
 @pytest.mark.parametrize("q_pos,L", [(32768, 32768), (32767, 32768), (5000, 33), (40, 1), (0, 1)])
 def test_host_decode_classifier_matches_oracle(q_pos, L):
-    for d_h, G, theta in ((128, 16, 1e6), (128, 32, 1e6), (64, 16, 1e3)):
+    for d_h, G, theta in ((128, 16, 1e6), (128, 32, 1e6), (64, 16, 1e3), (128, 2, 1e4), (64, 4, 1e3)):
         cut = [int(v) for v in O.group_cutoffs(theta, d_h, G)]
         got = W.decode_tile_counts(q_pos, L, d_h, G, cut)
         c, v = O.decode_tile_counts(q_pos, L, W.decode_tiling(d_h, G), np.array(cut))
@@ -240,7 +241,7 @@ def _prefill(**kw):
 def test_prefill_validation_codes():
     assert _prefill(q=None) == -1
     assert _prefill(d_h=96) == -3
-    assert _prefill(G=8) == -3
+    assert _prefill(G=12) == -3
     assert _prefill(Hq=3) == -2
     assert _prefill(n=0) == -2
     assert _prefill(q=ctypes.c_void_p(0x7F0000000008)) == -4
@@ -327,3 +328,22 @@ def test_backward_validation_codes():
     st = _strides(24)
     st[13] = 64                                          # dO token stride < d_h
     assert _backward(strides=st) == -2
+
+
+def test_fine_groups_scope():
+    # G = 2, 4, 8 (down to one cutoff per channel) run in prefill and decode;
+    # the backward pass and the compact K store take G = 16 or 32 only
+    for G in (2, 4, 8):
+        assert W.prefill_tiling(128, G) == (32, 64)
+        assert W.decode_tiling(64, G) == 32
+    assert _backward(G=8) == -3
+    assert _backward(G=2) == -3
+    L = W.lib()
+    caps = (ctypes.c_int32 * 64)()
+    offs = (ctypes.c_int64 * 65)()
+    cut = (ctypes.c_int32 * 64)(*range(64))
+    assert L.wp_kcache_layout(1000, 128, 2, cut, caps, offs) == -3
+    assert L.wp_kcache_layout(1000, 128, 8, cut, caps, offs) == -3
+    with pytest.raises(W.WPError) as e:
+        W.prefill_tiling(128, 12)
+    assert e.value.status == -3
