@@ -233,6 +233,60 @@ def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
                          "avg_ms": round(avg, 4)}}
 
 
+def bench_exact(W, qr, kr, v, dq, kc, vc, cl, qp, ws, od, theta, n, Hq, Hkv, d, Bd, L, q_pos,
+                grouped_prefill_ms, grouped_decode_ms):
+    """The exact per-channel rule (G = 2: every channel its own cutoff) on the
+    same prefill and decode workloads: 2 warmups, then 5 prefill / 20 decode
+    launches timed with events on the launch stream."""
+    import torch
+    log("bench: exact per-channel rule (G = 2)")
+    G2 = 2
+    cut2 = W.group_cutoffs(theta, d, G2)
+    o2 = torch.empty_like(qr)
+
+    def timed(fn, reps):
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in pairs]
+
+    pm = timed(lambda: W.prefill(qr, kr, v, cut2, G2, out=o2), 5)
+    dm = timed(lambda: W.decode(dq, kc, vc, cl, qp, cut2, G2, workspace=ws, out=od), 20)
+    dense_f, alg_f, _ = prefill_flops(n, Hq, 1, d, G2, cut2)
+    _, dec_alg, _ = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G2, cut2)
+    p_med, d_med = statistics.median(pm), statistics.median(dm)
+    p_avg, d_avg = sum(pm) / len(pm), sum(dm) / len(dm)
+    ach = alg_f / (p_avg * 1e-3) / 1e12
+    ach_d = dec_alg / (d_avg * 1e-3) / 1e9
+    return {"G": G2,
+            "prefill": {"ms_median": round(p_med, 4),
+                        "dense_equiv_tflops": round(dense_f / (p_med * 1e-3) / 1e12, 2),
+                        "algorithmic_tflops": round(alg_f / (p_med * 1e-3) / 1e12, 2),
+                        "algorithmic_fraction_of_dense": round(alg_f / dense_f, 4),
+                        "time_vs_grouped": round(p_med / grouped_prefill_ms, 4),
+                        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                                     "traffic": None, "kernel": "prefill_kernel<128,2>",
+                                     "avg_ms": round(p_avg, 4)}},
+            "decode": {"ms_median": round(d_med, 4),
+                       "algorithmic_gbs": round(dec_alg / (d_med * 1e-3) / 1e9, 1),
+                       "time_vs_grouped": round(d_med / grouped_decode_ms, 4),
+                       "roofline": {"bound": "hbm", "achieved": round(ach_d, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4), "traffic": None,
+                                    "algorithmic_bytes": dec_alg,
+                                    "kernel": "decode_split_kernel<128,2> + decode_merge_kernel<128>",
+                                    "avg_ms": round(d_avg, 4)}}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +297,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kcache", action="store_true", help="skip the compact K store decode line")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward line")
+    ap.add_argument("--no-exact", action="store_true", help="skip the exact per-channel rule (G = 2) line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches): a kernel of known "
                          "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -401,6 +456,9 @@ def main():
     if not args.no_kcache:
         out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kc, vc, cl, qp, cut, G, ws, od, dec_alg,
                                             med["decode"])
+    if not args.no_exact:
+        out["exact_rule"] = bench_exact(W, qr, kr, v, dqr[:, 0], kc, vc, cl, qp, ws, od, theta, n, Hq, Hkv, d,
+                                        Bd, L, q_pos, med["prefill"], med["decode"])
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)
