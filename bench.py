@@ -153,6 +153,10 @@ def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512
             done += 1
         dt = time.perf_counter() - t0
     done_rows = rows[:done]
+    # labelled extrapolation to the whole prefill: the oracle's cost per row
+    # grows with the row's causal length, so scale by sum(i + 1) over all rows
+    # / over the sampled rows
+    scale = (n * (n + 1) / 2.0) / float(np.sum(done_rows + 1))
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s (prefill, dense-equivalent)",
@@ -160,6 +164,8 @@ def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512
         "kind": "oracle",
         "sample": "%d seeded uniform query rows x %d heads of the 32K prefill "
                   "(grouped rule, float64 numpy, 1 BLAS thread), %.1f s" % (len(done_rows), Hq, dt),
+        "extrapolated_full_prefill_s": round(dt * scale, 1),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
     }
 
 
