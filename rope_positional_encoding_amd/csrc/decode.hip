@@ -139,13 +139,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   unsigned int cnt[CNG][3];
   unsigned int cnt_vis = 0;
   __shared__ unsigned int s_hist[(COUNT && FINE) ? 2 * (NG + 1) : 1];
+  // Fine groups: the cutoff table in LDS, and split points carried from
+  // block to block (a wave meets its key blocks in ascending order, so the
+  // distances and the split points only decrease).
+  __shared__ int s_cut[FINE ? NG : 1];
+  int fL = NG, fR = NG;
   if (COUNT) {
 #pragma unroll
     for (int g = 0; g < CNG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
     if constexpr (FINE) {
       if (tid < 2 * (NG + 1)) s_hist[tid] = 0;
-      __syncthreads();
     }
+  }
+  if constexpr (FINE) {
+    if (tid < NG) s_cut[tid] = a.cut[tid];
+    __syncthreads();
   }
   const float sl2 = a.scale_log2;
 
@@ -160,15 +168,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     const int jb1 = min(L, jb + 32) - 1;
     const int lD = qp - jb1;
     const int rD = qp - jb;
-    sL = 0;
-    sR = 0;
+    if constexpr (FINE) {
+      // idempotent for one block, so the load and the compute of a block
+      // may both call it
+      auto cut_at = [&](int g) { return __builtin_amdgcn_readfirstlane(s_cut[g]); };
+      while (fL > 0 && cut_at(fL - 1) >= lD) --fL;
+      while (fR > 0 && cut_at(fR - 1) >= rD) --fR;
+      sL = fL;
+      sR = fR;
+    } else {
+      sL = 0;
+      sR = 0;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      sL = (a.cut[g] < lD) ? g + 1 : sL;
-      sR = (a.cut[g] < rD) ? g + 1 : sR;
+      for (int g = 0; g < NG; ++g) {
+        sL = (a.cut[g] < lD) ? g + 1 : sL;
+        sR = (a.cut[g] < rD) ? g + 1 : sR;
+      }
+      sL = __builtin_amdgcn_readfirstlane(sL);
+      sR = __builtin_amdgcn_readfirstlane(sR);
     }
-    sL = __builtin_amdgcn_readfirstlane(sL);
-    sR = __builtin_amdgcn_readfirstlane(sR);
   };
 
   // issue every HBM load of one block: the kept K columns and all of V

@@ -193,6 +193,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const float sl2 = a.scale_log2;
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
+  // Fine groups (up to 64): the cutoff table in LDS, and split points
+  // carried from tile to tile.  A wave meets its key tiles in ascending
+  // order, so the tile distances, and with them splitL and splitR, only
+  // decrease; a few table reads per tile replace a 2 x 64-step scan.
+  __shared__ int s_cut[FINE ? NG : 1];
+  int fL = NG, fR = NG;
+  if constexpr (FINE) {
+    if (tid < NG) s_cut[tid] = a.cut[tid];
+  }
+  auto cut_at = [&](int g) { return __builtin_amdgcn_readfirstlane(s_cut[g]); };
+
   load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -210,13 +221,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       const int rD = i1w - j0;
       // cutoffs are non-decreasing: splitL / splitR = 1 + last group below
       int sL = 0, sR = 0;
+      if constexpr (FINE) {
+        while (fL > 0 && cut_at(fL - 1) >= lD) --fL;
+        while (fR > 0 && cut_at(fR - 1) >= rD) --fR;
+        sL = fL;
+        sR = fR;
+      } else {
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        sL = (a.cut[g] < lD) ? g + 1 : sL;
-        sR = (a.cut[g] < rD) ? g + 1 : sR;
+        for (int g = 0; g < NG; ++g) {
+          sL = (a.cut[g] < lD) ? g + 1 : sL;
+          sR = (a.cut[g] < rD) ? g + 1 : sR;
+        }
+        sL = __builtin_amdgcn_readfirstlane(sL);
+        sR = __builtin_amdgcn_readfirstlane(sR);
       }
-      sL = __builtin_amdgcn_readfirstlane(sL);
-      sR = __builtin_amdgcn_readfirstlane(sR);
       if (COUNT) {
         ++cnt_vis;
         if constexpr (FINE) {
