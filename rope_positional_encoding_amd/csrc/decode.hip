@@ -260,25 +260,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
           s[blk] = mfma16(R.k[blk][p], qr[p], s[blk]);
           continue;
         }
-        bool any_full = false;
-#pragma unroll
-        for (int gg = g_lo; gg <= g_hi; ++gg) any_full |= (gg >= sR);
+        const bool any_full = g_hi >= sR;          // the step's last group is full
         if (any_full) {
           const u32x4 op = FINE ? keep_words(R.k[blk][p], [&](int w) { return grp(w) >= sR; })
                                 : ((g >= sR) ? R.k[blk][p] : zero);
           s[blk] = mfma16(op, qr[p], s[blk]);
         }
+        if constexpr (FINE) {
+          // a runtime loop over just this step's partial groups: unrolled
+          // over all 32/G groups of every step the kernel outgrows the
+          // instruction cache
+#pragma unroll 1
+          for (int gg = max(g_lo, sL); gg < min(g_hi + 1, sR); ++gg) {
+            const u32x4 op = keep_words(R.k[blk][p], [&](int w) { return grp(w) == gg; });
+            const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
+            const int cg = __builtin_amdgcn_readfirstlane(s_cut[gg]);
 #pragma unroll
-        for (int gg = g_lo; gg <= g_hi; ++gg) {
-          if (gg < sL || gg >= sR) continue;       // only partial groups
-          const u32x4 op = FINE ? keep_words(R.k[blk][p], [&](int w) { return grp(w) == gg; })
-                                : ((g == gg) ? R.k[blk][p] : zero);
-          const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
-          const int cg = a.cut[gg];
+            for (int r = 0; r < 4; ++r) {
+              const int j = jb + 16 * blk + 4 * q4 + r;
+              s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+            }
+          }
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = jb + 16 * blk + 4 * q4 + r;
-            s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+          for (int gg = g_lo; gg <= g_hi; ++gg) {
+            if (gg < sL || gg >= sR) continue;     // only partial groups
+            const u32x4 op = (g == gg) ? R.k[blk][p] : zero;
+            const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
+            const int cg = a.cut[gg];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = jb + 16 * blk + 4 * q4 + r;
+              s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+            }
           }
         }
       }

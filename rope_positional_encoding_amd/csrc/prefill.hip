@@ -295,11 +295,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
               s0 = mfma32(keep_words(k0, [&](int w) { return grp(w) >= sR; }), qr[c], s0);
               s1 = mfma32(keep_words(k1, [&](int w) { return grp(w) >= sR; }), qr[c], s1);
             }
-#pragma unroll
-            for (int gi = 0; gi < 16 / G; ++gi) {
-              const int g = (16 * c) / G + gi;
-              if (g < sL || g >= sR) continue;
-              const int cg = a.cut[g];
+            // a runtime loop over just this step's partial groups (unrolled
+            // over all 16/G groups of every step, the code outgrows the
+            // instruction cache)
+#pragma unroll 1
+            for (int g = max((16 * c) / G, sL); g < min((16 * c + 15) / G + 1, sR); ++g) {
+              const int cg = cut_at(g);
               f32x16 t = mfma32(keep_words(k0, [&](int w) { return grp(w) == g; }), qr[c], zero16);
 #pragma unroll
               for (int r = 0; r < 16; ++r) s0[r] += (base - out_row(r, hh) <= cg) ? t[r] : 0.f;
