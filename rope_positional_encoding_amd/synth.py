@@ -141,6 +141,11 @@ WORKLOADS = {
                                1e6, 32, oracle_rows=256),
     "decode32k": Workload("decode32k", "decode", 4, 16, 32768, 32, 8, 128, 1e6, 16,
                           q_pos=32768),
+    # the same two shapes under the exact per-channel rule (G = 2)
+    "prefill32k_exact": Workload("prefill32k_exact", "prefill", 6, 1, 32768, 32, 8, 128,
+                                 1e6, 2, oracle_rows=256),
+    "decode32k_exact": Workload("decode32k_exact", "decode", 7, 16, 32768, 32, 8, 128,
+                                1e6, 2, q_pos=32768),
     "prefill128k_s4": Workload("prefill128k_s4", "prefill", 5, 1, 131072, 64, 8, 128,
                                1e6, 16, pos_scale=4.0, oracle_rows=128),
 }

@@ -80,10 +80,11 @@ def test_decode_split_count_invariance():
         assert (o.float() - base).abs().max().item() < 2e-2
 
 
-def test_workload_decode32k():
-    w = synth.WORKLOADS["decode32k"]
+@pytest.mark.parametrize("name", ["decode32k", "decode32k_exact"])
+def test_workload_decode32k(name):
+    w = synth.WORKLOADS[name]
     B, L, Hq, Hkv, d = w.B, w.n, w.Hq, w.Hkv, w.d_h
-    say("workload decode32k: B=%d L=%d Hq=%d Hkv=%d d=%d G=%d q_pos=%d" % (B, L, Hq, Hkv, d, w.G, w.q_pos))
+    say("workload %s: B=%d L=%d Hq=%d Hkv=%d d=%d G=%d q_pos=%d" % (name, B, L, Hq, Hkv, d, w.G, w.q_pos))
     with Timer("inputs"):
         q_raw = synth.normal_bits(w.seed, synth.TID_Q, B, (Hq, d))
         k_raw = synth.normal_bits(w.seed, synth.TID_K, B * L, (Hkv, d))
@@ -106,7 +107,9 @@ def test_workload_decode32k():
     exp = _expected([w.q_pos] * B, [L] * B, d, w.G, cut, Hkv)
     say("  counters", cnt.cpu().numpy().tolist())
     assert np.array_equal(cnt.cpu().numpy(), exp)
-    dim_cut = O.dim_cutoffs_grouped(np.array(cut), w.G)
+    # G = 2 is checked against the oracle's exact per-channel rule itself
+    dim_cut = (O.dim_cutoffs_exact(w.theta, d, w.pos_scale) if w.G == 2
+               else O.dim_cutoffs_grouped(np.array(cut), w.G))
     refs, dens = [], []
     with Timer("oracle"):
         for b in range(B):
@@ -117,5 +120,5 @@ def test_workload_decode32k():
             if b < 2:
                 dens.append(O.decode(qb, kb, vb, w.q_pos, L, O.dim_cutoffs_dense(d)))
     ref = np.stack(refs)
-    compare(got, ref, "decode32k O")
+    compare(got, ref, "%s O" % name)
     separation(ref[:2], np.stack(dens), "grouped vs dense (2 seqs)")

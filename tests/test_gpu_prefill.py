@@ -129,7 +129,9 @@ def _run_workload(name, nrows_override=None, sep_rows=0):
     got = bf16_to_np(o[0, torch.from_numpy(rows).to(dev())]).reshape(len(rows), w.Hq, w.d_h)
     del o, qr, kr, vd
     q_rows = q_raw[rows]
-    dim_cut = O.dim_cutoffs_grouped(np.array(cut), w.G)
+    # G = 2 is checked against the oracle's exact per-channel rule itself
+    dim_cut = (O.dim_cutoffs_exact(w.theta, w.d_h, w.pos_scale) if w.G == 2
+               else O.dim_cutoffs_grouped(np.array(cut), w.G))
     with Timer("oracle %d rows (x2)" % len(rows)):
         # bf16-in reference: the oracle's rotated q, k rounded to bf16, the
         # precision the attention kernel consumes
@@ -172,6 +174,10 @@ def test_workload_prefill4k():
 @pytest.mark.parametrize("name", ["prefill32k_g16", "prefill32k_g32"])
 def test_workload_prefill32k(name):
     _run_workload(name, sep_rows=16)
+
+
+def test_workload_prefill32k_exact():
+    _run_workload("prefill32k_exact", sep_rows=16)
 
 
 def test_workload_prefill128k_scaled():
