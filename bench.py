@@ -7,7 +7,10 @@ A step is one pass of the whole path over resident synthetic inputs:
   decode (16 sequences x 32K cached tokens, 32/8 heads).
 The in-house dense baseline (same kernels, every group full) is timed the
 same way right after, for the speedups.  Kernel times come from HIP events
-recorded on the stream the library launches on.
+recorded on the stream the library launches on.  The decode figures (and its
+roofline) come from the decode timed on its own as the pages time it (10
+warmups, median of 50 back-to-back launches, two cache copies alternating);
+the decode time inside the step, right after the prefill, is reported too.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -200,29 +203,22 @@ def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops):
             "speedup_vs_dense": round(res["dense"] / res["wp"], 4)}
 
 
-def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
+def bench_kcache(W, q, kcs, vcs, cl, qp, cut, G, ws, od, dec_alg, full_ms):
     """The same decode with K read from the group-major compact store (group
-    g keeps only its last D'_g + 1 keys): 10 warmups, median of 50."""
+    g keeps only its last D'_g + 1 keys), one store per cache copy, timed as
+    time_decode."""
     import torch
     log("bench: decode from the compact K store")
-    B, L, Hkv, d = kc.shape
-    store = W.kcache_empty(B, Hkv, L, d, G, cut, device=kc.device)
-    W.kcache_append(kc, torch.zeros(B, dtype=torch.int32, device=kc.device), store, L, cut, G)
-    for _ in range(10):
-        W.decode_kcache(q, store, vc, cl, qp, cut, G, workspace=ws, out=od)
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(50):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s = torch.cuda.current_stream()
-        e0.record(s)
-        W.decode_kcache(q, store, vc, cl, qp, cut, G, workspace=ws, out=od)
-        e1.record(s)
-        ts.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ts]
+    B, L, Hkv, d = kcs[0].shape
+    stores = []
+    for kc in kcs:
+        st = W.kcache_empty(B, Hkv, L, d, G, cut, device=kc.device)
+        W.kcache_append(kc, torch.zeros(B, dtype=torch.int32, device=kc.device), st, L, cut, G)
+        stores.append(st)
+    store = stores[0]
+    ms = time_decode(W, q, stores, vcs, cl, qp, cut, G, ws, od, compact=True)
     med = statistics.median(ms)
-    k_full = float(kc.numel() * 2)
+    k_full = float(kcs[0].numel() * 2)
     k_store = float(store.numel() * 2)
     avg = sum(ms) / len(ms)
     ach = dec_alg / (avg * 1e-3) / 1e9
@@ -239,23 +235,52 @@ def bench_kcache(W, q, kc, vc, cl, qp, cut, G, ws, od, dec_alg, full_ms):
                          "avg_ms": round(avg, 4)}}
 
 
-def bench_exact(W, qr, kr, v, dq, kc, vc, cl, qp, ws, od, theta, n, Hq, Hkv, d, Bd, L, q_pos,
+def time_decode(W, dq, kcs, vcs, cl, qp, cut, G, ws, od, dense=False, warmup=10, reps=50, compact=False):
+    """Decode timed on its own, as the pages time it: 10 warmups, then 50
+    launches with events on the launch stream and no host sync in between
+    (one untimed launch is queued first, so the host stays ahead of the GPU),
+    alternating between two copies of the KV cache.  Returns the times (ms)."""
+    import torch
+
+    def call(i):
+        if compact:
+            W.decode_kcache(dq, kcs[i & 1], vcs[i & 1], cl, qp, cut, G, workspace=ws, out=od)
+        else:
+            W.decode(dq, kcs[i & 1], vcs[i & 1], cl, qp, None if dense else cut, G, dense=dense,
+                     workspace=ws, out=od)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    call(1)
+    s = torch.cuda.current_stream()
+    pairs = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        call(i)
+        e1.record(s)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def bench_exact(W, qr, kr, v, dq, kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d, Bd, L, q_pos,
                 grouped_prefill_ms, grouped_decode_ms):
     """The exact per-channel rule (G = 2: every channel its own cutoff) on the
-    same prefill and decode workloads: 2 warmups, then 5 prefill / 20 decode
-    launches timed with events on the launch stream."""
+    same prefill and decode workloads: the prefill 2 warmups, then 5 launches
+    timed with events on the launch stream; the decode as time_decode over
+    the two cache copies kcs, vcs."""
     import torch
     log("bench: exact per-channel rule (G = 2)")
     G2 = 2
     cut2 = W.group_cutoffs(theta, d, G2)
     o2 = torch.empty_like(qr)
 
-    def timed(fn, reps, lead=None):
+    def timed(fn, reps):
         fn()
         fn()
         torch.cuda.synchronize()
-        if lead is not None:
-            lead()      # queued ahead (untimed) so the host is ahead of the GPU for short launches
         s = torch.cuda.current_stream()
         pairs = []
         for _ in range(reps):
@@ -268,8 +293,7 @@ def bench_exact(W, qr, kr, v, dq, kc, vc, cl, qp, ws, od, theta, n, Hq, Hkv, d, 
         return [a.elapsed_time(b) for a, b in pairs]
 
     pm = timed(lambda: W.prefill(qr, kr, v, cut2, G2, out=o2), 5)
-    dm = timed(lambda: W.decode(dq, kc, vc, cl, qp, cut2, G2, workspace=ws, out=od), 20,
-               lead=lambda: W.prefill(qr, kr, v, cut2, G2, out=o2))
+    dm = time_decode(W, dq, kcs, vcs, cl, qp, cut2, G2, ws, od)
     dense_f, alg_f, _ = prefill_flops(n, Hq, 1, d, G2, cut2)
     _, dec_alg, _ = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G2, cut2)
     p_med, d_med = statistics.median(pm), statistics.median(dm)
@@ -349,6 +373,7 @@ def main():
     dqr = torch.empty_like(dq_raw)
     kc = W.rope_apply(randn(Bd, L, Hkv, d), theta)     # the cache holds rotated keys
     vc = randn(Bd, L, Hkv, d)
+    kcs, vcs = (kc, kc.clone()), (vc, vc.clone())      # two cache copies for the decode loop
     od = torch.empty(Bd, Hq, d, dtype=torch.bfloat16, device=dev)
     cl = torch.full((Bd,), L, dtype=torch.int32, device=dev)
     qp = torch.full((Bd,), q_pos, dtype=torch.int32, device=dev)
@@ -398,6 +423,13 @@ def main():
 
     med = {k: statistics.median(v_) for k, v_ in per.items()}
     avg = {k: sum(v_) / len(v_) for k, v_ in per.items()}
+    # decode on its own (inside the step it follows the prefill, whose dirty
+    # output lines are written back to HBM during the decode)
+    log("bench: decode on its own")
+    dec_ms = time_decode(W, dqr[:, 0], kcs, vcs, cl, qp, cut, G, ws, od)
+    dec_ms_d = None if args.no_dense else time_decode(W, dqr[:, 0], kcs, vcs, cl, qp, cut, G, ws, od,
+                                                      dense=True)
+    dmed, davg = statistics.median(dec_ms), sum(dec_ms) / len(dec_ms)
     dense_f, alg_f, exe_f = prefill_flops(n, Hq, 1, d, G, cut)
     kv_dense, dec_alg, dec_issued = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G, cut)
     rope_bytes = 2 * 2.0 * (q_raw.numel() + k_raw.numel())
@@ -430,11 +462,14 @@ def main():
             "executed_fraction_of_dense": round(exe_f / dense_f, 4),
         },
         "decode": {
-            "ms_median": round(med["decode"], 4), "ms_min": round(min(per["decode"]), 4),
-            "kv_gbs_dense_equiv": round(kv_dense / (med["decode"] * 1e-3) / 1e9, 1),
-            "algorithmic_gbs": round(dec_alg / (med["decode"] * 1e-3) / 1e9, 1),
-            "issued_gbs": round(dec_issued / (med["decode"] * 1e-3) / 1e9, 1),
+            "protocol": "10 warmups, median of 50 back-to-back launches, two cache copies alternating",
+            "ms_median": round(dmed, 4), "ms_min": round(min(dec_ms), 4), "ms_max": round(max(dec_ms), 4),
+            "kv_gbs_dense_equiv": round(kv_dense / (dmed * 1e-3) / 1e9, 1),
+            "algorithmic_gbs": round(dec_alg / (dmed * 1e-3) / 1e9, 1),
+            "issued_gbs": round(dec_issued / (dmed * 1e-3) / 1e9, 1),
             "algorithmic_fraction_of_dense": round(dec_alg / kv_dense, 4),
+            "in_step_ms_median": round(med["decode"], 4),
+            "in_step_algorithmic_gbs": round(dec_alg / (med["decode"] * 1e-3) / 1e9, 1),
         },
         "rope": {"ms_q": round(med["rope_q"], 4), "ms_k": round(med["rope_k"], 4),
                  "gbs": round(rope_bytes / ((med["rope_q"] + med["rope_k"]) * 1e-3) / 1e9, 1)},
@@ -444,9 +479,12 @@ def main():
         out["prefill"]["dense_ms_median"] = round(med_d["prefill"], 4)
         out["prefill"]["dense_tflops"] = round(dense_f / (med_d["prefill"] * 1e-3) / 1e12, 2)
         out["prefill"]["speedup_vs_dense"] = round(med_d["prefill"] / med["prefill"], 4)
-        out["decode"]["dense_ms_median"] = round(med_d["decode"], 4)
-        out["decode"]["dense_kv_gbs"] = round(kv_dense / (med_d["decode"] * 1e-3) / 1e9, 1)
-        out["decode"]["speedup_vs_dense"] = round(med_d["decode"] / med["decode"], 4)
+        dmed_d = statistics.median(dec_ms_d)
+        out["decode"]["dense_ms_median"] = round(dmed_d, 4)
+        out["decode"]["dense_kv_gbs"] = round(kv_dense / (dmed_d * 1e-3) / 1e9, 1)
+        out["decode"]["speedup_vs_dense"] = round(dmed_d / dmed, 4)
+        out["decode"]["in_step_dense_ms_median"] = round(med_d["decode"], 4)
+        out["decode"]["in_step_speedup_vs_dense"] = round(med_d["decode"] / med["decode"], 4)
     # roofline of the dominant kernel (prefill): algorithmic FLOPs per launch
     # over the average launch duration measured with events on its stream
     ach = alg_f / (avg["prefill"] * 1e-3) / 1e12
@@ -454,20 +492,19 @@ def main():
                        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                        "traffic": measured_traffic("prefill"), "algorithmic_bytes": prefill_bytes,
                        "kernel": "prefill_kernel<128,16>", "avg_ms": round(avg["prefill"], 4)}
-    ach_d = dec_alg / (avg["decode"] * 1e-3) / 1e9
+    ach_d = dec_alg / (davg * 1e-3) / 1e9
     out["roofline_decode"] = {"bound": "hbm", "achieved": round(ach_d, 1), "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": round(ach_d / PEAK_HBM_GBS, 4),
                               "traffic": measured_traffic("decode"), "algorithmic_bytes": dec_alg,
                               "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
-                              "avg_ms": round(avg["decode"], 4)}
+                              "avg_ms": round(davg, 4)}
     if not args.no_backward:
         out["prefill_backward"] = bench_backward(W, qr, kr, v, cut, G, n, Hq, d, dense_f)
     if not args.no_kcache:
-        out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kc, vc, cl, qp, cut, G, ws, od, dec_alg,
-                                            med["decode"])
+        out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kcs, vcs, cl, qp, cut, G, ws, od, dec_alg, dmed)
     if not args.no_exact:
-        out["exact_rule"] = bench_exact(W, qr, kr, v, dqr[:, 0], kc, vc, cl, qp, ws, od, theta, n, Hq, Hkv, d,
-                                        Bd, L, q_pos, med["prefill"], med["decode"])
+        out["exact_rule"] = bench_exact(W, qr, kr, v, dqr[:, 0], kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d,
+                                        Bd, L, q_pos, med["prefill"], dmed)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)
