@@ -274,6 +274,52 @@ def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray
     return dq, dk, dv
 
 
+def prefill_backward_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                          dim_cut: np.ndarray, rows, key_from: int):
+    """The backward pass of prefill_backward for sizes where the n x n
+    matrices do not fit, restricted to a sample: dQ at the query rows `rows`,
+    and what those rows contribute to dK and dV of the keys j >= key_from.
+
+    Row by row, the same chain rule: with L_i the row's logits (logits()
+    above), P_i = softmax(L_i), dP_ij = dO_i . V_j and
+    dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij'):
+      dQ_id = (1/sqrt(d_h)) sum_{j <= i} dS_ij keep(i-j, d) k_jd
+      dK_jd += (1/sqrt(d_h)) dS_ij keep(i-j, d) q_id,   dV_j += P_ij dO_i.
+    A key only receives gradient from rows at or after it (causality), so
+    when `rows` holds every row >= key_from, the dK and dV returned are the
+    complete gradients of the keys j >= key_from.
+    Returns dq [len(rows), Hq, d_h], dk and dv [n - key_from, Hkv, d_h]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, Hq, d_h = q.shape
+    Hkv = k.shape[1]
+    r = Hq // Hkv
+    sc = 1.0 / math.sqrt(d_h)
+    cut = np.asarray(dim_cut, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((len(rows), Hq, d_h))
+    dk = np.zeros((n - key_from, Hkv, d_h))
+    dv = np.zeros((n - key_from, Hkv, d_h))
+    for idx, i in enumerate(rows):
+        dist = i - np.arange(i + 1)
+        keep = dist[:, None] <= cut[None, :]                           # [i+1, d_h]
+        for kv in range(Hkv):
+            hs = slice(kv * r, (kv + 1) * r)
+            L = logits(q[i, hs, :], k[: i + 1, kv, :], dist, cut)      # [r, i+1]
+            P = np.exp(L - L.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dP = do[i, hs, :] @ v[: i + 1, kv, :].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[idx, hs, :] = sc * (dS @ (k[: i + 1, kv, :] * keep))
+            if i >= key_from:
+                js = slice(key_from, i + 1)
+                dv[: i + 1 - key_from, kv, :] += P[:, js].T @ do[i, hs, :]
+                dk[: i + 1 - key_from, kv, :] += sc * (dS[:, js].T @ q[i, hs, :]) * keep[js]
+    return dq, dk, dv
+
+
 # ----------------------------------------------------------------------------
 # tile classification
 # ----------------------------------------------------------------------------

@@ -88,3 +88,33 @@ def test_backward_finite_differences():
             args2 = [a2 if arr is x else x for x in (q, k, v)]
             fd = (loss(*args1) - loss(*args2)) / (2 * eps)
             assert abs(fd - grad[idx]) < 1e-7 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,d,table,key_from", [
+    (40, 4, 1, 16, "grouped", 30),
+    (33, 2, 2, 32, "exact", 20),
+    (21, 2, 1, 16, "dense", 0),
+])
+def test_backward_rows_matches_autograd(n, Hq, Hkv, d, table, key_from):
+    """prefill_backward_rows (the row-sampled backward used at full sizes)
+    against torch autograd of the forward written above: dQ at scattered
+    rows, dK and dV of the keys >= key_from from every row >= key_from."""
+    rng = np.random.default_rng(11 + n)
+    q = rng.standard_normal((n, Hq, d))
+    k = rng.standard_normal((n, Hkv, d))
+    v = rng.standard_normal((n, Hkv, d))
+    do = rng.standard_normal((n, Hq, d))
+    theta = 40.0
+    if table == "dense":
+        cut = O.dim_cutoffs_dense(d)
+    elif table == "exact":
+        cut = O.dim_cutoffs_exact(theta, d)
+    else:
+        cut = O.dim_cutoffs_grouped(O.group_cutoffs(theta, d, 8), 8)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    (_torch_forward(tq, tk, tv, cut) * torch.tensor(do)).sum().backward()
+    rows = np.array(sorted({0, 3, n // 2} | set(range(key_from, n))))
+    dq, dk, dv = O.prefill_backward_rows(q, k, v, do, cut, rows, key_from)
+    assert np.allclose(dq, tq.grad.numpy()[rows], rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk, tk.grad.numpy()[key_from:], rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, tv.grad.numpy()[key_from:], rtol=1e-10, atol=1e-12)
