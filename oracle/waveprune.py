@@ -12,7 +12,7 @@ arXiv 2610.06963):
   [article] kongchang.com article "WavePrune：RoPE只用一个旋转周期，长文本性能反而更好"
   [thread]  the first author's thread on sotwe.com (tweets 3/7 and 6/7)
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   * channel c is the interleaved pair of dims (2c, 2c+1) ([article], RoPE
     paragraph: the pair (q_{2i}, q_{2i+1}));
   * the 2x2 rotation is [[cos, -sin], [sin, cos]] applied to (x, y);
