@@ -122,3 +122,35 @@ def test_workload_decode32k(name):
     ref = np.stack(refs)
     compare(got, ref, "%s O" % name)
     separation(ref[:2], np.stack(dens), "grouped vs dense (2 seqs)")
+
+
+def test_decode_empty_sequences():
+    """A sequence with an empty cache (cache_len 0) gets o = 0 exactly and
+    visits no key block; the sequences around it are unaffected."""
+    B, Lmax, Hq, Hkv, d, G, theta = 4, 200, 8, 2, 128, 16, 1e3
+    lens = [0, 37, 0, 200]
+    say("decode empty sequences: lens=%s" % lens)
+    q = synth.normal_bits(31, 0, B, (Hq, d))
+    kc = synth.normal_bits(31, 1, B * Lmax, (Hkv, d))
+    vc = synth.normal_bits(31, 2, B * Lmax, (Hkv, d))
+    cut = W.group_cutoffs(theta, d, G)
+    qt = bits_to_dev(q, (B, Hq, d))
+    kt = bits_to_dev(kc, (B, Lmax, Hkv, d))
+    vt = bits_to_dev(vc, (B, Lmax, Hkv, d))
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    qp = torch.tensor(lens, dtype=torch.int32, device=dev())
+    cnt = torch.zeros(3 * (d // G) + 1, dtype=torch.int64, device=dev())
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=dev())
+    o = W.decode(qt, kt, vt, cl, qp, cut, G, counters=cnt, out=out, num_splits=3)
+    torch.cuda.synchronize()
+    got = bf16_to_np(o)
+    dim_cut = O.dim_cutoffs_grouped(np.array(cut), G)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(got[b], np.zeros((Hq, d))), b
+        else:
+            sl = slice(b * Lmax, b * Lmax + Lmax)
+            ref = O.decode(to_f64(q[b]), to_f64(kc[sl]), to_f64(vc[sl]), L, L, dim_cut)
+            compare(got[b], ref, "decode b=%d L=%d" % (b, L))
+    exp = _expected(lens, lens, d, G, cut, Hkv)
+    assert np.array_equal(cnt.cpu().numpy(), exp)
