@@ -249,9 +249,11 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cutoffs: Optional
 
 def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                      dout: torch.Tensor, lse: torch.Tensor, cutoffs: Optional[Sequence[int]], G: int,
-                     dense: bool = False, workspace: Optional[torch.Tensor] = None):
+                     dense: bool = False, workspace: Optional[torch.Tensor] = None,
+                     out: Optional[Sequence[torch.Tensor]] = None):
     """Gradients (dq, dk, dv) of <dout, o> for wp_prefill's inputs; o and lse
-    [B, Hq, n] (natural log) from the forward pass."""
+    [B, Hq, n] (natural log) from the forward pass.  out: optional (dq, dk,
+    dv) tensors (views allowed) to write into."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _need(t, nm, torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
@@ -265,9 +267,16 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     need = lib().wp_prefill_backward_workspace_size(B, n, Hq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
-    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
-    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    if out is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    else:
+        dq, dk, dv = out
+        for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _need(t, nm, torch.bfloat16, 4)
+        if tuple(dq.shape) != (B, n, Hq, d) or tuple(dk.shape) != (B, n, Hkv, d) or tuple(dv.shape) != (B, n, Hkv, d):
+            raise ValueError("out must be (dq [B, n, Hq, d_h], dk [B, n, Hkv, d_h], dv [B, n, Hkv, d_h])")
     strides = []
     for t in (q, k, v, o, dout, dq, dk, dv):
         strides += list(t.stride()[:3])

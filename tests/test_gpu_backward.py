@@ -122,3 +122,28 @@ def test_backward_workload_32k():
             % (name, err.max(), err.mean(), scale, err.max() / scale, err.mean() / scale))
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (name, err.max(), err.mean())
         assert err.mean() <= 4e-3 * scale, (name, err.mean() / scale)
+
+
+def test_backward_strided_views():
+    """q, k, v as views into one packed [B, n, Hq + 2 Hkv, d] projection
+    output, dO as a view into a wider tensor, and dQ, dK, dV written into one
+    packed gradient buffer: bit-identical to the contiguous call, the
+    buffer's padding untouched."""
+    B, n, Hq, Hkv, d, G = 2, 333, 8, 2, 128, 16
+    x = [synth.normal_bits(53, t, B * n, (h, d)) for t, h in ((0, Hq), (1, Hkv), (2, Hkv), (3, Hq))]
+    qt, kt, vt, gt = (bits_to_dev(a, (B, n, a.shape[1], d)) for a in x)
+    cut = W.group_cutoffs(300.0, d, G)
+    o, lse = W.prefill(qt, kt, vt, cut, G, return_lse=True)
+    r1 = W.prefill_backward(qt, kt, vt, o, gt, lse, cut, G)
+    H = Hq + 2 * Hkv
+    qkv = torch.cat([qt, kt, vt], dim=2)                  # [B, n, H, d]
+    gw = torch.zeros((B, n, Hq + 2, d), dtype=torch.bfloat16, device=dev())
+    gw[:, :, 1:1 + Hq] = gt
+    grad = torch.zeros((B, n, H + 2, d), dtype=torch.bfloat16, device=dev())
+    dq, dk, dv = (grad[:, :, 1:1 + Hq], grad[:, :, 1 + Hq:1 + Hq + Hkv], grad[:, :, 1 + Hq + Hkv:1 + H])
+    r2 = W.prefill_backward(qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:], o,
+                            gw[:, :, 1:1 + Hq], lse, cut, G, out=(dq, dk, dv))
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.count_nonzero(grad[:, :, 0]) == 0 and torch.count_nonzero(grad[:, :, 1 + H]) == 0

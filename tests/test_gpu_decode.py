@@ -154,3 +154,31 @@ def test_decode_empty_sequences():
             compare(got[b], ref, "decode b=%d L=%d" % (b, L))
     exp = _expected(lens, lens, d, G, cut, Hkv)
     assert np.array_equal(cnt.cpu().numpy(), exp)
+
+
+def test_decode_strided_views():
+    """K and V as views into one interleaved cache [B, Lmax, 2, Hkv, d] (the
+    layout of frameworks that keep K and V of a token together), q as a view
+    into a wider tensor and o written into a wider buffer: bit-identical to
+    the contiguous call, and the buffer outside o untouched."""
+    B, Lmax, Hq, Hkv, d, G, theta = 3, 700, 16, 4, 128, 16, 300.0
+    lens = [700, 513, 64]
+    q = synth.normal_bits(41, 0, B, (Hq, d))
+    kc = synth.normal_bits(41, 1, B * Lmax, (Hkv, d))
+    vc = synth.normal_bits(41, 2, B * Lmax, (Hkv, d))
+    cut = W.group_cutoffs(theta, d, G)
+    qt = bits_to_dev(q, (B, Hq, d))
+    kt = bits_to_dev(kc, (B, Lmax, Hkv, d))
+    vt = bits_to_dev(vc, (B, Lmax, Hkv, d))
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    qp = torch.tensor(lens, dtype=torch.int32, device=dev())
+    o1 = W.decode(qt, kt, vt, cl, qp, cut, G, num_splits=4)
+    kv = torch.stack([kt, vt], dim=2)                     # [B, Lmax, 2, Hkv, d]
+    qwide = torch.zeros((B, Hq + 3, d), dtype=torch.bfloat16, device=dev())
+    qwide[:, 1:1 + Hq] = qt
+    big = torch.zeros((B, Hq + 5, d), dtype=torch.bfloat16, device=dev())
+    o2 = W.decode(qwide[:, 1:1 + Hq], kv[:, :, 0], kv[:, :, 1], cl, qp, cut, G, num_splits=4,
+                  out=big[:, 2:2 + Hq])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.count_nonzero(big[:, :2]) == 0 and torch.count_nonzero(big[:, 2 + Hq:]) == 0
