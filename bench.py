@@ -478,10 +478,13 @@ def main():
         med_d = {k: statistics.median(v_) for k, v_ in per_d.items()}
         out["prefill"]["dense_ms_median"] = round(med_d["prefill"], 4)
         out["prefill"]["dense_tflops"] = round(dense_f / (med_d["prefill"] * 1e-3) / 1e12, 2)
+        # the dense baseline executes every FLOP it is credited with: its own fraction of the MFMA peak
+        out["prefill"]["dense_frac_of_peak"] = round(dense_f / (med_d["prefill"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         out["prefill"]["speedup_vs_dense"] = round(med_d["prefill"] / med["prefill"], 4)
         dmed_d = statistics.median(dec_ms_d)
         out["decode"]["dense_ms_median"] = round(dmed_d, 4)
         out["decode"]["dense_kv_gbs"] = round(kv_dense / (dmed_d * 1e-3) / 1e9, 1)
+        out["decode"]["dense_frac_of_peak"] = round(kv_dense / (dmed_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out["decode"]["speedup_vs_dense"] = round(dmed_d / dmed, 4)
         out["decode"]["in_step_dense_ms_median"] = round(med_d["decode"], 4)
         out["decode"]["in_step_speedup_vs_dense"] = round(med_d["decode"] / med["decode"], 4)
