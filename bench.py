@@ -266,10 +266,11 @@ def time_decode(W, dq, kcs, vcs, cl, qp, cut, G, ws, od, dense=False, warmup=10,
 
 
 def bench_exact(W, qr, kr, v, dq, kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d, Bd, L, q_pos,
-                grouped_prefill_ms, grouped_decode_ms):
+                grouped_prefill_ms, grouped_decode_ms, grouped_backward_ms=None):
     """The exact per-channel rule (G = 2: every channel its own cutoff) on the
     same prefill and decode workloads: the prefill 2 warmups, then 5 launches
-    timed with events on the launch stream; the decode as time_decode over
+    timed with events on the launch stream (the backward, when the grouped
+    one was timed, 2 warmups and 3 launches); the decode as time_decode over
     the two cache copies kcs, vcs."""
     import torch
     log("bench: exact per-channel rule (G = 2)")
@@ -293,6 +294,11 @@ def bench_exact(W, qr, kr, v, dq, kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d
         return [a.elapsed_time(b) for a, b in pairs]
 
     pm = timed(lambda: W.prefill(qr, kr, v, cut2, G2, out=o2), 5)
+    bm = None
+    if grouped_backward_ms is not None:
+        _, lse2 = W.prefill(qr, kr, v, cut2, G2, out=o2, return_lse=True)
+        g = torch.randn(qr.shape, device=qr.device, dtype=torch.float32).to(torch.bfloat16)
+        bm = timed(lambda: W.prefill_backward(qr, kr, v, o2, g, lse2, cut2, G2), 3)
     dm = time_decode(W, dq, kcs, vcs, cl, qp, cut2, G2, ws, od)
     dense_f, alg_f, _ = prefill_flops(n, Hq, 1, d, G2, cut2)
     _, dec_alg, _ = decode_bytes(L, q_pos, Hkv, Hq, Bd, d, G2, cut2)
@@ -300,7 +306,7 @@ def bench_exact(W, qr, kr, v, dq, kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d
     p_avg, d_avg = sum(pm) / len(pm), sum(dm) / len(dm)
     ach = alg_f / (p_avg * 1e-3) / 1e12
     ach_d = dec_alg / (d_avg * 1e-3) / 1e9
-    return {"G": G2,
+    out = {"G": G2,
             "prefill": {"ms_median": round(p_med, 4),
                         "dense_equiv_tflops": round(dense_f / (p_med * 1e-3) / 1e12, 2),
                         "algorithmic_tflops": round(alg_f / (p_med * 1e-3) / 1e12, 2),
@@ -318,6 +324,11 @@ def bench_exact(W, qr, kr, v, dq, kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d
                                     "algorithmic_bytes": dec_alg,
                                     "kernel": "decode_split_kernel<128,2> + decode_merge_kernel<128>",
                                     "avg_ms": round(d_avg, 4)}}}
+    if bm is not None:
+        b_med = statistics.median(bm)
+        out["prefill_backward"] = {"ms_median": round(b_med, 3),
+                                   "time_vs_grouped": round(b_med / grouped_backward_ms, 4)}
+    return out
 
 
 def main():
@@ -501,13 +512,15 @@ def main():
                               "traffic": measured_traffic("decode"), "algorithmic_bytes": dec_alg,
                               "kernel": "decode_split_kernel<128,16> + decode_merge_kernel<128>",
                               "avg_ms": round(davg, 4)}
+    bwd_ms = None
     if not args.no_backward:
         out["prefill_backward"] = bench_backward(W, qr, kr, v, cut, G, n, Hq, d, dense_f)
+        bwd_ms = out["prefill_backward"]["ms_median"]
     if not args.no_kcache:
         out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kcs, vcs, cl, qp, cut, G, ws, od, dec_alg, dmed)
     if not args.no_exact:
         out["exact_rule"] = bench_exact(W, qr, kr, v, dqr[:, 0], kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d,
-                                        Bd, L, q_pos, med["prefill"], dmed)
+                                        Bd, L, q_pos, med["prefill"], dmed, bwd_ms)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)

@@ -29,12 +29,12 @@
  *    caller's next synchronization of `stream`.
  *  - Supported: d_h in {64, 128}; Hq a multiple of Hkv; G in {16, 32}
  *    everywhere, and also G in {2, 4, 8} for the tiling / tile-count
- *    queries, wp_prefill and wp_decode.  G = 2 gives every channel its own
- *    cutoff: the exact per-channel rule of [notes] section 2.1, Eq. (6),
- *    which section 2.3 approximates by groups (kept for quality ablations;
- *    a tile mixing classes inside one 16-dim MFMA step costs extra masked
- *    MFMAs).  wp_prefill_backward and the compact K store (wp_kcache_*,
- *    wp_decode_kcache) take G in {16, 32} only (WP_ERR_UNSUPPORTED
+ *    queries, wp_prefill, wp_prefill_backward and wp_decode.  G = 2 gives
+ *    every channel its own cutoff: the exact per-channel rule of [notes]
+ *    section 2.1, Eq. (6), which section 2.3 approximates by groups (kept
+ *    for quality ablations; a tile mixing classes inside one 16-dim MFMA
+ *    step costs extra masked MFMAs).  The compact K store (wp_kcache_*,
+ *    wp_decode_kcache) takes G in {16, 32} only (WP_ERR_UNSUPPORTED
  *    otherwise).
  */
 #ifndef WAVEPRUNE_H

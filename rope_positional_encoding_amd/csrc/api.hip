@@ -480,7 +480,7 @@ wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const
   if (flags & ~WP_FLAG_DENSE) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
   const bool dense = flags & WP_FLAG_DENSE;
   if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
-  if (!supported_coarse(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
   if (B < 1 || n < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, n, Hq, Hkv must be >= 1");
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};

@@ -170,7 +170,8 @@ __device__ inline void bare_barrier() {
 template <int D, int G>
 __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   constexpr int NCH = D / 16;
-  constexpr int GC = G / 16;
+  constexpr bool FINE = G < 16;                   // several groups per 16-dim MFMA step
+  constexpr int GC = FINE ? 1 : G / 16;
   constexpr int NG = D / G;
   constexpr int ND = D / 32;
   constexpr int RB = D * 2;
@@ -185,11 +186,21 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2 * TILE_B];
   __shared__ __attribute__((aligned(256))) float s_ld[kStages][64];
   __shared__ __attribute__((aligned(16))) float s_p[2][4][16 * 64];
+  // fine groups: the cutoff table, read with wave-uniform indexes
+  __shared__ int s_cut[FINE ? NG : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave & 3;
+  if constexpr (FINE) {
+    if (tid < NG) s_cut[tid] = a.cut[tid];
+  }
+  auto cut_at = [&](int g) { return __builtin_amdgcn_readfirstlane(s_cut[g]); };
+  // fine groups: split points carried from tile to tile.  Within one query
+  // head a wave meets its query tiles in ascending order, so the distances
+  // and the split points only grow; they restart at the head's first tile.
+  int fL = 0, fR = 0;
   const bool pwave = wave < 4;                     // forms P and dV (else dP, dS, dK)
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -306,15 +317,56 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     const int v = PW ? u : u - 1;
     const int i0 = __builtin_amdgcn_readfirstlane((t0 + cti) * 32);
     const int i1 = min(n, i0 + 32) - 1;
+    if (FINE && cti == 0) {
+      fL = 0;
+      fR = 0;
+    }
     if (!(v >= 0 && v < total && wave_valid && i1 >= key0)) return;
     const int lD = max(0, i0 - key1);
     const int rD = i1 - key0;
     int sL, sR;
-    split_points<NG>(a.cut, lD, rD, sL, sR);
+    if constexpr (FINE) {
+      while (fL < NG && cut_at(fL) < lD) ++fL;
+      while (fR < NG && cut_at(fR) < rD) ++fR;
+      sL = fL;
+      sR = fR;
+    } else {
+      split_points<NG>(a.cut, lD, rD, sL, sR);
+    }
     auto rop = [&](const unsigned char* t, int c) { return *reinterpret_cast<const u32x4*>(t + rread[c]); };
     if constexpr (PW) {
       // ---- S = Q K^T: full groups [sR, NG) as one chain, then partials ----
       f32x16 s = zero16;
+      if constexpr (FINE) {
+        // steps [c_end, NCH) hold full groups only: one chain; steps
+        // [c_lo, c_end) mix classes: their full groups join with the other
+        // dims of the K operand zeroed, each partial group gets its own
+        // masked MFMA (a run-time loop over just the step's partial groups)
+        const int c_end = (sR * G + 15) / 16;
+        const int c_lo = (sL * G) / 16;
+        if (c_end < NCH) {
+          s = mfma32(rop(sq, NCH - 1), br[NCH - 1], zero16);
+#pragma unroll
+          for (int cc = NCH - 2; cc >= 0; --cc) {
+            if (cc < c_end) break;
+            s = mfma32(rop(sq, cc), br[cc], s);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (c < c_lo || c >= c_end) continue;
+          const u32x4 qa = rop(sq, c);
+          auto grp = [&](int w) { return (16 * c + 8 * hh + 2 * w) / G; };
+          if ((16 * c + 15) / G >= sR) s = mfma32(qa, keep_words(br[c], [&](int w) { return grp(w) >= sR; }), s);
+#pragma unroll 1
+          for (int g = max((16 * c) / G, sL); g < min((16 * c + 15) / G + 1, sR); ++g) {
+            const int cg = cut_at(g);
+            const f32x16 t = mfma32(qa, keep_words(br[c], [&](int w) { return grp(w) == g; }), zero16);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= cg) ? t[r] : 0.f;
+          }
+        }
+      } else {
       if (sR < NG) {
         s = mfma32(rop(sq, NCH - 1), br[NCH - 1], zero16);
 #pragma unroll
@@ -333,6 +385,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] += (i0 + out_row(r, hh) - jkey <= a.cut[g]) ? t[r] : 0.f;
         }
+      }
       }
       // ---- P, to the partner and packed; queries before the key or past
       //      the end are masked, on the tiles that have such queries ----
@@ -411,6 +464,29 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
       }
       // partial groups [sL, sR): dS masked by the group's cutoff, A rows of
       // the group only
+      if constexpr (FINE) {
+        // per 32-dim block, a run-time loop over its partial groups
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const int g_lo = max(sL, (32 * db) / G), g_hi = min(sR, (32 * db + 31) / G + 1);
+          if (g_lo >= g_hi) continue;
+          const u32x2 lo0 = read_tr16(sq + tlo[db]);
+          const u32x2 hi0 = read_tr16(sq + thi[db]);
+          const u32x2 lo1 = read_tr16(sq + 16 * RB + tlo[db]);
+          const u32x2 hi1 = read_tr16(sq + 16 * RB + thi[db]);
+          const u32x4 q0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+          const u32x4 q1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+          const int gl = (32 * db + l32) / G;           // group of this lane's A row
+#pragma unroll 1
+          for (int g = g_lo; g < g_hi; ++g) {
+            u32x4 bop[2] = {dsp[0], dsp[1]};
+            const int cg = cut_at(g);
+            mask_block(bop, [&](int r) { return i0 + out_row(r, hh) - jkey <= cg; });
+            acc[db] = mfma32(gl == g ? q0 : zero4, bop[0], acc[db]);
+            acc[db] = mfma32(gl == g ? q1 : zero4, bop[1], acc[db]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g < sL || g >= sR) continue;
@@ -427,6 +503,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
         const u32x4 a1 = mine ? u32x4{lo1[0], lo1[1], hi1[0], hi1[1]} : zero4;
         acc[db] = mfma32(a0, bop[0], acc[db]);
         acc[db] = mfma32(a1, bop[1], acc[db]);
+      }
       }
     }
   };
@@ -510,7 +587,8 @@ constexpr int kDqThreads = 64 * kDqWaves;
 template <int D, int G>
 __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int NCH = D / 16;
-  constexpr int GC = G / 16;
+  constexpr bool FINE = G < 16;                   // several groups per 16-dim MFMA step
+  constexpr int GC = FINE ? 1 : G / 16;
   constexpr int NG = D / G;
   constexpr int ND = D / 32;
   constexpr int RB = D * 2;
@@ -522,12 +600,21 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
 
   // [stage][K tile | V tile]
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE_B];
+  // fine groups: the cutoff table, read with wave-uniform indexes
+  __shared__ int s_cut[FINE ? NG : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  if constexpr (FINE) {
+    if (tid < NG) s_cut[tid] = a.cut[tid];
+  }
+  auto cut_at = [&](int g) { return __builtin_amdgcn_readfirstlane(s_cut[g]); };
+  // fine groups: split points carried from tile to tile (the key tiles come
+  // in ascending order, so the distances and the split points only shrink)
+  int fL = NG, fR = NG;
   const int QSUB = kDqWaves / a.HPW;
   const int QB = 32 * QSUB;
   const int nqb = (a.n + QB - 1) / QB;
@@ -647,7 +734,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
     if (wave_valid && j0 <= i1w) {
       const int j1 = min(n - 1, j0 + 63);
       int sL, sR;
-      split_points<NG>(a.cut, max(0, i0w - j1), i1w - j0, sL, sR);
+      if constexpr (FINE) {
+        const int lD = max(0, i0w - j1), rD = i1w - j0;
+        while (fL > 0 && cut_at(fL - 1) >= lD) --fL;
+        while (fR > 0 && cut_at(fR - 1) >= rD) --fR;
+        sL = fL;
+        sR = fR;
+      } else {
+        split_points<NG>(a.cut, max(0, i0w - j1), i1w - j0, sL, sR);
+      }
       auto kop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c]); };
       auto vop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sv + kb * 32 * RB + vread[c]); };
       const int base = qi - j0;                    // distance = base - (32kb + out_row(r))
@@ -658,6 +753,34 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
         // ---- S^T = K Q^T: full groups as one chain, then partials ----
         f32x16 s = zero16;
+        if constexpr (FINE) {
+          // as in the dK/dV kernel: a chain over the all-full steps, then
+          // the mixed steps with operand words zeroed per group
+          const int c_end = (sR * G + 15) / 16;
+          const int c_lo = (sL * G) / 16;
+          if (c_end < NCH) {
+            s = mfma32(kop(kb, NCH - 1), qr[NCH - 1], zero16);
+#pragma unroll
+            for (int cc = NCH - 2; cc >= 0; --cc) {
+              if (cc < c_end) break;
+              s = mfma32(kop(kb, cc), qr[cc], s);
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            if (c < c_lo || c >= c_end) continue;
+            const u32x4 ka = kop(kb, c);
+            auto grp = [&](int w) { return (16 * c + 8 * hh + 2 * w) / G; };
+            if ((16 * c + 15) / G >= sR) s = mfma32(ka, keep_words(qr[c], [&](int w) { return grp(w) >= sR; }), s);
+#pragma unroll 1
+            for (int g = max((16 * c) / G, sL); g < min((16 * c + 15) / G + 1, sR); ++g) {
+              const int cg = cut_at(g);
+              const f32x16 t = mfma32(ka, keep_words(qr[c], [&](int w) { return grp(w) == g; }), zero16);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s[r] += (base - 32 * kb - out_row(r, hh) <= cg) ? t[r] : 0.f;
+            }
+          }
+        } else {
         if (sR < NG) {
           s = mfma32(kop(kb, NCH - 1), qr[NCH - 1], zero16);
 #pragma unroll
@@ -676,6 +799,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] += (base - 32 * kb - out_row(r, hh) <= a.cut[g]) ? t[r] : 0.f;
           }
+        }
         }
         // ---- dP^T = V dO^T ----
         f32x16 dp = mfma32(vop(kb, 0), gr[0], zero16);
@@ -699,6 +823,46 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
       }
 
       // ---- dQ^T += K^T dS^T, masked per group ----
+      if constexpr (FINE) {
+        // per 32-dim block: its full groups with unmasked dS^T and the A rows
+        // (dims) of other groups zeroed, then a run-time loop over its
+        // partial groups, each with dS^T masked by the group's cutoff and
+        // the A rows of the group only
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
+          if (gb < sL) continue;                     // every group of the block skipped
+          const int gl = (32 * db + l32) / G;        // group of this lane's A row
+          u32x4 ka[4];
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const u32x2 lo = read_tr16(sk + kc * 16 * RB + tlo[db]);
+            const u32x2 hi = read_tr16(sk + kc * 16 * RB + thi[db]);
+            ka[kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+          if (gb >= sR) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) dqt[db] = mfma32(gl >= sR ? ka[kc] : zero4, dsp[kc], dqt[db]);
+          }
+#pragma unroll 1
+          for (int g = max(ga, sL); g < min(gb + 1, sR); ++g) {
+            const int cg = cut_at(g);
+            u32x4 bop[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              f32x16 dm;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) dm[r] = (base - 32 * kb - out_row(r, hh) <= cg) ? dsv[kb][r] : 0.f;
+              u32x4 pk[2];
+              pack_block(dm, pk);
+              bop[2 * kb] = pk[0];
+              bop[2 * kb + 1] = pk[1];
+            }
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) dqt[db] = mfma32(gl == g ? ka[kc] : zero4, bop[kc], dqt[db]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
         const int ga = (32 * db) / G, gb = (32 * db + 31) / G;
@@ -741,6 +905,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
             }
           }
         }
+      }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -786,6 +951,12 @@ hipError_t launch_backward(const BackwardArgs& a, int d_h, int G, hipStream_t s)
   if (d_h == 128 && G == 32) return launch_bwd<128, 32>(a, s);
   if (d_h == 64 && G == 16) return launch_bwd<64, 16>(a, s);
   if (d_h == 64 && G == 32) return launch_bwd<64, 32>(a, s);
+  if (d_h == 128 && G == 8) return launch_bwd<128, 8>(a, s);
+  if (d_h == 128 && G == 4) return launch_bwd<128, 4>(a, s);
+  if (d_h == 128 && G == 2) return launch_bwd<128, 2>(a, s);
+  if (d_h == 64 && G == 8) return launch_bwd<64, 8>(a, s);
+  if (d_h == 64 && G == 4) return launch_bwd<64, 4>(a, s);
+  if (d_h == 64 && G == 2) return launch_bwd<64, 2>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -331,13 +331,15 @@ def test_backward_validation_codes():
 
 
 def test_fine_groups_scope():
-    # G = 2, 4, 8 (down to one cutoff per channel) run in prefill and decode;
-    # the backward pass and the compact K store take G = 16 or 32 only
+    # G = 2, 4, 8 (down to one cutoff per channel) run in prefill, decode and
+    # the backward pass; the compact K store takes G = 16 or 32 only
     for G in (2, 4, 8):
         assert W.prefill_tiling(128, G) == (32, 64)
         assert W.decode_tiling(64, G) == 32
-    assert _backward(G=8) == -3
-    assert _backward(G=2) == -3
+        # the group size is accepted: validation stops at the small workspace
+        cutg = (ctypes.c_int32 * (128 // G))(*range(128 // G))
+        assert _backward(G=G, cut=cutg, ws_bytes=1024) == -5
+    assert _backward(G=12, cut=(ctypes.c_int32 * 64)(*range(64))) == -3
     L = W.lib()
     caps = (ctypes.c_int32 * 64)()
     offs = (ctypes.c_int64 * 65)()

@@ -2,10 +2,11 @@
 
 The GPU gradients use the GPU forward's bf16 O and float LSE, bf16 P and dS
 MFMA operands and float accumulation, and are rounded to bf16; the oracle
-works in float64 from the same bf16 inputs.  Gate per tensor: the absolute
-gate of the forward output (max-abs <= 2e-2, mean-abs <= 2e-3; the gradients
-here have mean magnitudes 0.07-0.25, like O), and a mean-abs error <= 4e-3
-relative to the tensor's mean magnitude.  The relative floor, from emulating
+works in float64 from the same bf16 inputs.  Gate per tensor: the gate of
+the forward output (max-abs <= 2e-2, scaled by the tensor's largest entry
+where that exceeds 1; mean-abs <= 2e-3; the gradients here have mean
+magnitudes 0.07-0.25, like O), and a mean-abs error <= 4e-3 relative to the
+tensor's mean magnitude.  The relative floor, from emulating
 the roundings in float64 on the CPU: bf16 output rounding alone gives
 1.4e-3, with bf16 P (or dS) operands 2.1e-3; the kernels measure 2.1-2.4e-3.
 """
@@ -30,6 +31,14 @@ CASES = [
     (1, 200, 4, 1, 128, 16, 1e4, True),
     (1, 161, 6, 2, 128, 16, 50.0, False),
     (1, 2048, 4, 1, 128, 16, 1e4, False),          # many tiles at a realistic theta
+    # fine groups: G = 2 is the exact per-channel rule; small thetas put many
+    # channels in the partial class on one tile
+    (1, 300, 4, 2, 128, 2, 300.0, False),
+    (2, 257, 8, 2, 128, 4, 1e3, False),
+    (1, 400, 4, 1, 128, 8, 50.0, False),
+    (1, 333, 4, 4, 64, 2, 100.0, False),
+    (1, 200, 2, 1, 64, 8, 1e4, False),
+    (1, 1000, 8, 2, 128, 2, 1e4, False),
 ]
 
 
@@ -54,7 +63,12 @@ def test_backward_matches_oracle(B, n, Hq, Hkv, d, G, theta, dense):
     dq, dk, dv = W.prefill_backward(qt, kt, vt, o, gt, lse, None if dense else cut, G, dense=dense)
     torch.cuda.synchronize()
     got = [bf16_to_np(x).reshape(B, n, x.shape[2], d) for x in (dq, dk, dv)]
-    dim_cut = O.dim_cutoffs_dense(d) if dense else O.dim_cutoffs_grouped(np.array(cut), G)
+    if dense:
+        dim_cut = O.dim_cutoffs_dense(d)
+    elif G == 2:
+        dim_cut = O.dim_cutoffs_exact(theta, d)      # G = 2 against the exact rule itself
+    else:
+        dim_cut = O.dim_cutoffs_grouped(np.array(cut), G)
     for b in range(B):
         sl = slice(b * n, (b + 1) * n)
         ref = O.prefill_backward(to_f64(q[sl]), to_f64(k[sl]), to_f64(v[sl]), to_f64(g[sl]), dim_cut)
@@ -66,7 +80,11 @@ def test_backward_matches_oracle(B, n, Hq, Hkv, d, G, theta, dense):
             errs.append((name, mx, mean))
         for (name, mx, mean), gg, rr in zip(errs, got, ref):
             err = np.abs(gg[b] - rr)
-            assert err.max() <= 2e-2 and err.mean() <= 2e-3, (name, err.max(), err.mean())
+            # the max-abs gate scales with the tensor's largest entry once that
+            # exceeds 1 (bf16 rounding alone is 2^-9 of the value; dK and dV
+            # sum over the GQA heads and grow past O's range)
+            assert err.max() <= 2e-2 * max(1.0, np.abs(rr).max()), (name, err.max(), np.abs(rr).max())
+            assert err.mean() <= 2e-3, (name, err.mean())
             assert mean <= 4e-3, (name, mean)
 
 
