@@ -1,7 +1,6 @@
 """GPU parity of prefill, decode and the backward with cutoff tables from
-general sources:
-a per-channel scaled frequency vector, alpha != 2, and truncation of only
-the first channels (wp_cutoffs_from_freqs).  The kernels take any
+general sources: a per-channel scaled frequency vector, alpha != 2, and
+truncation of only the first channels (wp_cutoffs_from_freqs).  The kernels take any
 non-decreasing table; these cases check the table end to end against the
 oracle's own general-cutoff path (all rows, max-abs 2e-2 / mean-abs 2e-3,
 tile counters bit-exact)."""
