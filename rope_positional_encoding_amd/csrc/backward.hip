@@ -584,8 +584,12 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
 constexpr int kDqWaves = 4;
 constexpr int kDqThreads = 64 * kDqWaves;
 
+// Two workgroups per CU, except for G = 2 (one cutoff per channel), whose
+// per-group loops need more than 256 registers: it runs at one workgroup per
+// CU without spilling (measured 4% faster than two with spills; G = 4, 8 are
+// faster at two).
 template <int D, int G>
-__global__ __launch_bounds__(kDqThreads, 2) void bwd_dq_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(kDqThreads, G == 2 ? 1 : 2) void bwd_dq_kernel(BackwardArgs a) {
   constexpr int NCH = D / 16;
   constexpr bool FINE = G < 16;                   // several groups per 16-dim MFMA step
   constexpr int GC = FINE ? 1 : G / 16;
