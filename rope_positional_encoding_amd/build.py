@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwaveprune.so")
+CHECK = os.path.join(ROOT, "tests", "c_abi_check")
 SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -54,6 +55,9 @@ def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    # the tests' standalone C++ user of the C ABI (host code only, no torch)
+    _run([HIPCC, *COMMON, os.path.join(ROOT, "tests", "c_abi_check.cpp"), "-o", CHECK, "-L", PKG,
+          "-lwaveprune", "-Wl,-rpath,$ORIGIN/../rope_positional_encoding_amd"], verbose)
     return LIB
 
 
