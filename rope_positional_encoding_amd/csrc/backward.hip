@@ -37,6 +37,13 @@
 //    one MFMA per 16-row k step; otherwise each non-skipped group takes its
 //    own MFMA with the A rows of the other group zeroed and its own (masked)
 //    dS operand.
+//  * Fine groups (G = 2, 4, 8; G = 2 is the exact per-channel rule): a
+//    16-dim MFMA step of the logits holds several groups, so the steps that
+//    mix classes take their full groups with the other operand words zeroed
+//    and each partial group in a masked MFMA of its own; a 32-row block of
+//    dK^T / dQ^T takes its full groups in one MFMA set and its partial groups
+//    in a run-time loop (unrolled over up to 16 groups per block, the code
+//    would outgrow the instruction cache).
 #include "wp_device.h"
 #include "wp_internal.h"
 
