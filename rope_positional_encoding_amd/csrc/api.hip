@@ -387,7 +387,6 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
     return fail(WP_ERR_UNSUPPORTED, "the compact K store takes G = 16 or 32 (G=%d)", G);
   if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, Lmax, Hq, Hkv must be >= 1");
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
-  if (Hq / Hkv > 16) return fail(WP_ERR_UNSUPPORTED, "decode supports at most 16 query heads per kv head");
   if (num_splits < 0) return fail(WP_ERR_ARG, "num_splits must be >= 0");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v_cache) || !aligned16(o))
     return fail(WP_ERR_ALIGN, "q, the K cache or store, v_cache, o must be 16-byte aligned");
@@ -441,15 +440,26 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
   a.ks_b = st10[2]; a.ks_t = st10[3]; a.ks_h = st10[4];
   a.vs_b = st10[5]; a.vs_t = st10[6]; a.vs_h = st10[7];
   a.os_b = st10[8]; a.os_h = st10[9];
-  a.B = B; a.Lmax = Lmax; a.Hq = Hq; a.Hkv = Hkv;
-  a.r = Hq / Hkv;
+  a.B = B; a.Lmax = Lmax; a.Hkv = Hkv;
+  a.rs = Hq / Hkv;
   a.S = S;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d_h));
   const long long blocks = (long long)B * Hkv * S;
   if (blocks > 2147483647LL || (long long)B * Hq > 2147483647LL)
     return fail(WP_ERR_SHAPE, "grid too large");
-  hipError_t e = wp::launch_decode(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(WP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  // The kernel holds at most 16 query heads of a kv head as MFMA columns.
+  // More heads per kv head run in passes of 16 (each pass reads the cache
+  // again; tile counts are taken in the first pass only); the passes share
+  // the workspace in stream order.
+  for (int h0 = 0; h0 < a.rs; h0 += 16) {
+    wp::DecodeArgs p = a;
+    p.r = a.rs - h0 < 16 ? a.rs - h0 : 16;
+    p.Hq = Hkv * p.r;
+    p.q = a.q + (int64_t)h0 * a.qs_h;
+    p.o = a.o + (int64_t)h0 * a.os_h;
+    hipError_t e = wp::launch_decode(p, d_h, G, count && h0 == 0, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 }  // namespace

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   u32x4 qr[NP];
   {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bf16* qb = a.q + (int64_t)b * a.qs_b + (int64_t)(kvh * a.r + n16) * a.qs_h + q4 * 8;
+    const bf16* qb = a.q + (int64_t)b * a.qs_b + (int64_t)(kvh * a.rs + n16) * a.qs_h + q4 * 8;
 #pragma unroll
     for (int p = 0; p < NP; ++p)
       qr[p] = (n16 < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
@@ -445,13 +445,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-// One wave per (sequence, query head): O = sum_s 2^(m_s - m*) o_s /
-// sum_s 2^(m_s - m*) l_s.
+// One wave per (sequence, query head of this launch): O = sum_s 2^(m_s - m*)
+// o_s / sum_s 2^(m_s - m*) l_s.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
+  const int kvh = h / a.r;
+  const int ho = kvh * a.rs + (h - kvh * a.r);    // the head's index among the model's heads
   const int lane = threadIdx.x;
   const int64_t base = (int64_t)bh * a.S;
   float mm = -INFINITY;
@@ -471,7 +473,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     }
   }
   const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-  bf16* op = a.o + (int64_t)b * a.os_b + (int64_t)h * a.os_h;
+  bf16* op = a.o + (int64_t)b * a.os_b + (int64_t)ho * a.os_h;
 #pragma unroll
   for (int e = 0; e < PER; ++e) op[lane + 64 * e] = static_cast<__bf16>(acc[e] * inv);
 }

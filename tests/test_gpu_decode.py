@@ -182,3 +182,38 @@ def test_decode_strided_views():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.count_nonzero(big[:, :2]) == 0 and torch.count_nonzero(big[:, 2 + Hq:]) == 0
+
+
+# B, Lmax, Hq, Hkv, d, G, theta, cache lengths, splits
+WIDE_GQA = [
+    (2, 900, 32, 1, 128, 16, 1e3, [900, 451], 0),      # 32 query heads on one kv head: two passes
+    (1, 1500, 40, 2, 64, 32, 300.0, [1500], 3),         # 20 per kv head: passes of 16 and 4
+    (2, 700, 48, 2, 128, 2, 1e4, [700, 1], 0),          # 24 per kv head, exact rule
+]
+
+
+@pytest.mark.parametrize("B,Lmax,Hq,Hkv,d,G,theta,lens,splits", WIDE_GQA)
+def test_decode_wide_gqa(B, Lmax, Hq, Hkv, d, G, theta, lens, splits):
+    """More than 16 query heads per kv head (MQA-style): the heads run in
+    passes of 16 over the same cache; every head against the oracle and the
+    tile counters counted once per (sequence, kv head, key block)."""
+    say("decode wide GQA: B=%d Lmax=%d Hq=%d Hkv=%d d=%d G=%d lens=%s" % (B, Lmax, Hq, Hkv, d, G, lens))
+    q = synth.normal_bits(47, 0, B, (Hq, d))
+    kc = synth.normal_bits(47, 1, B * Lmax, (Hkv, d))
+    vc = synth.normal_bits(47, 2, B * Lmax, (Hkv, d))
+    cut = W.group_cutoffs(theta, d, G)
+    qt = bits_to_dev(q, (B, Hq, d))
+    kt = bits_to_dev(kc, (B, Lmax, Hkv, d))
+    vt = bits_to_dev(vc, (B, Lmax, Hkv, d))
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    qp = torch.tensor(lens, dtype=torch.int32, device=dev())
+    cnt = torch.zeros(3 * (d // G) + 1, dtype=torch.int64, device=dev())
+    o = W.decode(qt, kt, vt, cl, qp, cut, G, counters=cnt, num_splits=splits)
+    torch.cuda.synchronize()
+    got = bf16_to_np(o)
+    dim_cut = O.dim_cutoffs_exact(theta, d) if G == 2 else O.dim_cutoffs_grouped(np.array(cut), G)
+    for b in range(B):
+        sl = slice(b * Lmax, (b + 1) * Lmax)
+        ref = O.decode(to_f64(q[b]), to_f64(kc[sl]), to_f64(vc[sl]), lens[b], lens[b], dim_cut)
+        compare(got[b], ref, "decode wide GQA b=%d" % b)
+    assert np.array_equal(cnt.cpu().numpy(), _expected(lens, lens, d, G, cut, Hkv))
