@@ -269,6 +269,16 @@ def _decode(**kw):
     return W.lib().wp_decode(*args.values())
 
 
+def test_decode_largest_cache_span():
+    # 2^20 keys at a 2 KB token stride end 2 KB short of 2^31 bytes and pass
+    # validation (stopped here by the small workspace); one key more is
+    # rejected (the K/V buffer resources address 32 bits)
+    st = _strides(10)
+    st[3] = st[6] = 8 * 128                              # k_t, v_t in elements
+    assert _decode(B=1, Lmax=1 << 20, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -5
+    assert _decode(B=1, Lmax=(1 << 20) + 1, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -2
+
+
 def test_decode_validation_codes():
     assert _decode(ws=None) == -1
     assert _decode(d_h=80) == -3
