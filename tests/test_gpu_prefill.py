@@ -182,3 +182,31 @@ def test_workload_prefill32k_exact():
 
 def test_workload_prefill128k_scaled():
     _run_workload("prefill128k_s4")
+
+
+def test_prefill_largest_kv_span():
+    """K and V at the largest span the 32-bit buffer addressing takes: 4096
+    tokens at a 512 KB token stride (views of one head out of 2048), so the
+    last key of the sequence ends 0.5 MB short of 2^31 bytes.  Sampled rows
+    against the oracle, counters bit-exact."""
+    n, Hq, Hkv, Hall, d, G, theta = 4096, 4, 1, 2048, 128, 16, 1e4
+    say("prefill largest span: n=%d token stride %d bytes" % (n, Hall * d * 2))
+    assert (n - 1) * Hall * d * 2 + 2 * d < 2 ** 31 - 1
+    q = synth.normal_bits(91, 0, n, (Hq, d))
+    k = synth.normal_bits(91, 1, n, (Hkv, d))
+    v = synth.normal_bits(91, 2, n, (Hkv, d))
+    qt = bits_to_dev(q, (1, n, Hq, d))
+    kbig = torch.zeros((1, n, Hall, d), dtype=torch.bfloat16, device=dev())
+    vbig = torch.zeros((1, n, Hall, d), dtype=torch.bfloat16, device=dev())
+    kbig[:, :, Hall - 1:] = bits_to_dev(k, (1, n, Hkv, d))       # the last head: the far end of the buffer
+    vbig[:, :, Hall - 1:] = bits_to_dev(v, (1, n, Hkv, d))
+    cut = W.group_cutoffs(theta, d, G)
+    cnt = _counters(d, G)
+    o = W.prefill(qt, kbig[:, :, Hall - 1:], vbig[:, :, Hall - 1:], cut, G, counters=cnt)
+    torch.cuda.synchronize()
+    del kbig, vbig
+    rows = synth.sample_rows(n, 96, 91, [c + e for c in cut for e in (0, 1)])
+    got = bf16_to_np(o[0, torch.from_numpy(rows).to(dev())]).reshape(len(rows), Hq, d)
+    ref = O.prefill(to_f64(q), to_f64(k), to_f64(v), O.dim_cutoffs_grouped(np.array(cut), G), rows=rows)
+    compare(got, ref, "prefill largest span (%d rows)" % len(rows))
+    assert np.array_equal(cnt.cpu().numpy(), _expected_counts(n, d, G, cut, Hq))
