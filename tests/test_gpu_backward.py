@@ -165,3 +165,39 @@ def test_backward_strided_views():
     for a, b in zip(r1, r2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.count_nonzero(grad[:, :, 0]) == 0 and torch.count_nonzero(grad[:, :, 1 + H]) == 0
+
+
+def test_backward_largest_span():
+    """q, k, v and dO as head views at a 512 KB token stride, 4096 tokens:
+    every input sequence ends just short of 2^31 bytes from its first row,
+    the most the 32-bit buffer addressing takes.  dQ at sampled rows and the
+    last 48 rows, dK and dV at the last 48 keys, against the oracle."""
+    n, Hq, Hkv, Hall, d, G, theta = 4096, 4, 1, 2048, 128, 16, 1e4
+    tail = 48
+    say("backward largest span: n=%d token stride %d bytes" % (n, Hall * d * 2))
+    x = [synth.normal_bits(97, t, n, (h, d)) for t, h in ((0, Hq), (1, Hkv), (2, Hkv), (3, Hq))]
+    views = []
+    bigs = []
+    for a, h in zip(x, (Hq, Hkv, Hkv, Hq)):
+        big = torch.zeros((1, n, Hall, d), dtype=torch.bfloat16, device=dev())
+        big[:, :, Hall - h:] = bits_to_dev(a, (1, n, h, d))
+        bigs.append(big)
+        views.append(big[:, :, Hall - h:])
+    qt, kt, vt, gt = views
+    assert (n - 1) * Hall * d * 2 + 2 * d * Hq < 2 ** 31 - 1
+    cut = W.group_cutoffs(theta, d, G)
+    o, lse = W.prefill(qt, kt, vt, cut, G, return_lse=True)
+    dq, dk, dv = W.prefill_backward(qt, kt, vt, o, gt, lse, cut, G)
+    torch.cuda.synchronize()
+    key_from = n - tail
+    rows = np.union1d(synth.sample_rows(n, 32, 97, [c + e for c in cut for e in (0, 1)]), np.arange(key_from, n))
+    got = (bf16_to_np(dq[0, torch.from_numpy(rows).to(dev())]).reshape(len(rows), Hq, d),
+           bf16_to_np(dk[0, key_from:]).reshape(tail, Hkv, d), bf16_to_np(dv[0, key_from:]).reshape(tail, Hkv, d))
+    del bigs, views, qt, kt, vt, gt
+    ref = O.prefill_backward_rows(*(to_f64(a) for a in x), O.dim_cutoffs_grouped(np.array(cut), G), rows, key_from)
+    for nm, gg, rr in zip(("dQ rows", "dK tail", "dV tail"), got, ref):
+        err = np.abs(gg - rr)
+        scale = np.abs(rr).mean()
+        say("  %s: max-abs %.2e mean-abs %.2e (mean |ref| %.3g)" % (nm, err.max(), err.mean(), scale))
+        assert err.max() <= 2e-2 * max(1.0, np.abs(rr).max()) and err.mean() <= 2e-3, nm
+        assert err.mean() <= 4e-3 * scale, (nm, err.mean() / scale)
