@@ -99,6 +99,7 @@ CASES = [
     (3, 1200, 16, 4, 64, 32, 100.0, [1200, 64, 1], 1, 3),
     (2, 3000, 32, 8, 128, 16, 1e3, [3000, 2047], -1, 0),
     (1, 4096, 8, 1, 128, 32, 300.0, [4096], 0, 5),
+    (2, 900, 32, 1, 128, 16, 100.0, [900, 17], 0, 0),    # 32 query heads on one kv head: passes of 16
 ]
 
 

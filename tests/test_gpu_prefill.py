@@ -40,6 +40,7 @@ SMALL = [
     (1, 513, 16, 2, 128, 16, 1e6, 4.0),
     (1, 300, 4, 4, 64, 16, 30.0, 1.0),
     (3, 161, 8, 2, 128, 16, 300.0, 1.0),
+    (1, 500, 32, 1, 128, 16, 100.0, 1.0),       # MQA: 32 query heads on one kv head
 ]
 
 
