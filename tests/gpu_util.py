@@ -94,15 +94,29 @@ def round_bf16_f64(x: np.ndarray) -> np.ndarray:
     return synth.bf16_round(x.astype(np.float32)).astype(np.float64)
 
 
-def oracle_prefill_rows(w, q_raw_rows, k_raw, v_bits, rows, dim_cut, b=0, bf16_in=False):
+def oracle_prefill_rows(w, q_raw_rows, k_raw, v_bits, rows, dim_cut, b=0, bf16_in=False, threads=8):
     """Oracle output rows [len(rows), Hq, d] of batch b: RoPE in float64 of the
     raw inputs at positions 0..n-1, then the rule given by dim_cut.  With
     bf16_in, the rotated q and k are rounded to bf16 (nearest even) first:
-    the precision the attention kernel takes its inputs in."""
+    the precision the attention kernel takes its inputs in.  The rows are
+    independent, so they are dealt to `threads` host threads (one BLAS
+    thread each); the oracle itself is unchanged."""
     n = w.n
+    rows = np.asarray(rows)
     kr = O.rope(to_f64(k_raw[b * n:(b + 1) * n]), np.arange(n), w.theta, w.pos_scale)
-    qr = O.rope(to_f64(q_raw_rows), np.asarray(rows), w.theta, w.pos_scale)
+    qr = O.rope(to_f64(q_raw_rows), rows, w.theta, w.pos_scale)
     if bf16_in:
         kr, qr = round_bf16_f64(kr), round_bf16_f64(qr)
     v = to_f64(v_bits[b * n:(b + 1) * n])
-    return O.prefill(qr, kr, v, dim_cut, rows=rows, q_is_rows=True)
+    if threads <= 1 or len(rows) < 4 * threads:
+        return O.prefill(qr, kr, v, dim_cut, rows=rows, q_is_rows=True)
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    # interleaved chunks balance the causal lengths
+    parts = [np.arange(t, len(rows), 4 * threads) for t in range(4 * threads)]
+    out = np.zeros((len(rows),) + qr.shape[1:])
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        res = ex.map(lambda ix: O.prefill(qr[ix], kr, v, dim_cut, rows=rows[ix], q_is_rows=True), parts)
+        for ix, r in zip(parts, res):
+            out[ix] = r
+    return out
