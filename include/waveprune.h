@@ -302,6 +302,30 @@ int32_t wp_decode_num_splits(int32_t B, int32_t Lmax, int32_t Hkv);
 size_t wp_decode_workspace_size(int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv,
                                 int32_t d_h, int32_t num_splits);
 
+/*
+ * wp_decode_noalloc -- wp_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, kernels and results as wp_decode
+ * (bit-identical for the same num_splits), but the per-split partial
+ * results live in a fixed device array inside the library instead of a
+ * caller workspace: WP_DECODE_SCRATCH_BYTES (8 MiB) on each GPU, held from
+ * the first call on that GPU until the process ends.  The call allocates and
+ * frees nothing (no hipMalloc, hipFree or allocating library routine).
+ * Errors: WP_ERR_WORKSPACE when wp_decode_workspace_size(B, Lmax, Hq, Hkv,
+ * d_h, num_splits) exceeds WP_DECODE_SCRATCH_BYTES (e.g. at d_h = 128,
+ * B * Hq * splits above about 16000); WP_ERR_HIP if the array's device
+ * address cannot be looked up; otherwise the errors of wp_decode.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on different streams, or from
+ * different threads) race and must be ordered by the caller.
+ */
+#define WP_DECODE_SCRATCH_BYTES (8u << 20)
+wp_status wp_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            const int32_t* cache_len, const int32_t* q_pos,
+                            int32_t B, int32_t Lmax, int32_t Hq, int32_t Hkv, int32_t d_h,
+                            const int64_t strides[10], const int32_t* cutoffs, int32_t G,
+                            int32_t num_splits, uint32_t flags, int64_t* counters, void* stream);
+
 /* The classification tile of the prefill kernel: BM queries x BN keys. */
 wp_status wp_prefill_tiling(int32_t d_h, int32_t G, int32_t* BM, int32_t* BN);
 

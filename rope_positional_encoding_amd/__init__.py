@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "WPError", "lib", "group_cutoffs", "rope_apply", "prefill", "decode",
+    "WPError", "lib", "group_cutoffs", "rope_apply", "prefill", "decode", "decode_noalloc",
     "decode_num_splits", "decode_workspace_size", "prefill_tiling", "decode_tiling",
     "prefill_tile_counts", "decode_tile_counts", "FLAG_DENSE", "FLAG_COUNT", "NEVER_PRUNE",
 ]
@@ -47,6 +47,8 @@ _SIGNATURES = {
                           _u32, _vp, _vp]),
     "wp_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P, _i32,
                          _i32, _vp, _sz, _u32, _vp, _vp]),
+    "wp_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P,
+                                 _i32, _i32, _u32, _vp, _vp]),
     "wp_kcache_layout": (_i32, [_i32, _i32, _i32, _I32P, _I32P, _I64P]),
     "wp_kcache_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _I64P, _vp, _vp, _I64P, _i32, _I32P, _i32, _vp]),
     "wp_decode_kcache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _I64P, _I32P,
@@ -318,6 +320,35 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_len), _ptr(q_pos), B, Lmax, Hq,
         Hkv, d, _i64arr(strides), cut, int(G), int(num_splits), _ptr(workspace),
         workspace.numel() * workspace.element_size(), flags, _ptr(counters), _stream(q)))
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cache_len: torch.Tensor, q_pos: torch.Tensor, cutoffs: Optional[Sequence[int]], G: int,
+                   dense: bool = False, num_splits: int = 0, counters: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """wp_decode_noalloc: decode with the partial results in the library's
+    fixed device scratch (no workspace).  With `out` given, the call
+    allocates nothing on the device."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(q_pos, "q_pos", torch.int32, 1)
+    B, Hq, d = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Lmax, Hkv, d) or tuple(v_cache.shape) != (B, Lmax, Hkv, d):
+        raise ValueError("k_cache and v_cache must be [B, Lmax, Hkv, d_h]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    flags = (FLAG_DENSE if dense else 0) | (FLAG_COUNT if counters is not None else 0)
+    cut = None if cutoffs is None else _cut(cutoffs, d, G)
+    strides = (list(q.stride()[:2]) + list(k_cache.stride()[:3]) + list(v_cache.stride()[:3])
+               + list(out.stride()[:2]))
+    _check(lib().wp_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(cache_len), _ptr(q_pos), B, Lmax, Hq,
+        Hkv, d, _i64arr(strides), cut, int(G), int(num_splits), flags, _ptr(counters), _stream(q)))
     return out
 
 

@@ -475,6 +475,29 @@ wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, voi
                      num_splits, workspace, workspace_bytes, flags, counters, stream, false);
 }
 
+wp_status wp_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            const int32_t* cache_len, const int32_t* q_pos, int32_t B, int32_t Lmax,
+                            int32_t Hq, int32_t Hkv, int32_t d_h, const int64_t strides[10],
+                            const int32_t* cutoffs, int32_t G, int32_t num_splits, uint32_t flags,
+                            int64_t* counters, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !cache_len || !q_pos || !strides)
+    return fail(WP_ERR_NULL, "a required pointer is NULL");
+  if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d_h < 1)
+    return fail(WP_ERR_SHAPE, "B, Lmax, Hq, Hkv, d_h must be >= 1");
+  if (num_splits < 0) return fail(WP_ERR_ARG, "num_splits must be >= 0");
+  const size_t need = wp_decode_workspace_size(B, Lmax, Hq, Hkv, d_h, num_splits);
+  if (need > wp::kDecodeScratchBytes)
+    return fail(WP_ERR_WORKSPACE,
+                "the partial results need %zu bytes, more than the %zu-byte device scratch of "
+                "wp_decode_noalloc (use wp_decode with a workspace, or fewer splits)",
+                need, wp::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = wp::decode_scratch(&scratch);
+  if (e != hipSuccess) return fail(WP_ERR_HIP, "decode scratch address: %s", hipGetErrorString(e));
+  return decode_impl(q, k_cache, v_cache, o, cache_len, q_pos, B, Lmax, Hq, Hkv, d_h, strides, cutoffs, G,
+                     num_splits, scratch, wp::kDecodeScratchBytes, flags, counters, stream, false);
+}
+
 size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq) {
   if (B < 1 || n < 1 || Hq < 1) return 0;
   return align256((size_t)B * Hq * n * 2 * sizeof(float));

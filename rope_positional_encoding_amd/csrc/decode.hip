@@ -24,6 +24,8 @@
 //    (keys permuted to match), so the A operand is one 16-byte LDS read.
 //  * The 4 waves merge through LDS at the end; a second kernel merges the
 //    splits (log-sum-exp weighted), one wave per (sequence, query head).
+#include <mutex>
+
 #include "wp_device.h"
 #include "wp_internal.h"
 
@@ -526,6 +528,33 @@ __global__ __launch_bounds__(256) void kcache_append_kernel(KAppendArgs a) {
 }
 
 }  // namespace
+
+// Partial results of the decode entry point that allocates nothing: one
+// file-scope array per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// for the symbol); it uses the device address from hipGetSymbolAddress.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // with this device current: its own copy of the array, at its own address
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s) {
   if (d_h == 128 && G == 16) return launch_dgc<128, 16>(a, count, s);

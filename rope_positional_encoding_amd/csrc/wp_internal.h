@@ -137,6 +137,12 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_kcache_append(const KAppendArgs& a, hipStream_t s);
+
+// Size of the decode scratch array of each GPU (the allocation-free decode
+// entry point keeps its partial results there), and its device address on
+// the current device, looked up once per device.
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;   // WP_DECODE_SCRATCH_BYTES
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_backward(const BackwardArgs& a, int d_h, int G, hipStream_t s);
 
 }  // namespace wp
