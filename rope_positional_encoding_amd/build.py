@@ -58,7 +58,35 @@ def build(verbose: bool = False, extra=()) -> str:
     # the tests' standalone C++ user of the C ABI (host code only, no torch)
     _run([HIPCC, *COMMON, os.path.join(ROOT, "tests", "c_abi_check.cpp"), "-o", CHECK, "-L", PKG,
           "-lwaveprune", "-Wl,-rpath,$ORIGIN/../rope_positional_encoding_amd"], verbose)
+    build_host_check(verbose)
     return LIB
+
+
+# The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer,
+# linked with host stand-ins of the kernel launchers (tests/host_check/), for
+# the CPU tests.  The sanitizers apply to host code only (-Xarch_host); the
+# link is a host-only step.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_CHECK = os.path.join(ROOT, "tests", "host_check", "host_check")
+
+
+def build_host_check(verbose: bool = False) -> str:
+    out = os.path.join(BUILD, "san")
+    os.makedirs(out, exist_ok=True)
+    flags = ["--offload-arch=gfx950", "-O1", "-g", "-fPIC", "-std=c++17", *SAN_HOST,
+             "-I", os.path.join(ROOT, "include")]
+    srcs = [os.path.join(CSRC, "api.hip"), os.path.join(ROOT, "tests", "host_check", "launch_stubs.cpp"),
+            os.path.join(ROOT, "tests", "host_check", "host_check.cpp")]
+    objs = [os.path.join(out, os.path.basename(s).split(".")[0] + ".o") for s in srcs]
+    for s, o in zip(srcs, objs):
+        _run([HIPCC, *flags, "-c", s, "-o", o], verbose)
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    _run([clang, "-fsanitize=address,undefined", *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
+          "-o", HOST_CHECK], verbose)
+    return HOST_CHECK
 
 
 if __name__ == "__main__":
