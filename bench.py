@@ -125,51 +125,226 @@ def measured_traffic(kernel):
 
 
 # ---------------------------------------------------------------------------
-def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=512):
-    """The CPU oracle (as it stands) on seeded uniform query rows of the same
-    32K prefill (the rotated inputs the GPU consumed), single BLAS thread;
-    scaled to dense-equivalent TFLOP/s."""
+def _oracle_threads():
+    """Host threads for the oracle: the CPUs this process may run on (at
+    most 16, the host share of one GPU on the box)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _timed_rows(fn, items, threads, budget_s=None):
+    """Run fn(item) over items on `threads` host threads (one BLAS thread
+    each), stopping at budget_s seconds if given; returns (done_items,
+    seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    done = []
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        if threads <= 1:
+            for it in items:
+                fn(it)
+                done.append(it)
+                if budget_s is not None and time.perf_counter() - t0 > budget_s and len(done) >= 4:
+                    break
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                pos = 0
+                while pos < len(items):
+                    batch = items[pos:pos + 4 * threads]
+                    list(ex.map(fn, batch))
+                    done.extend(batch)
+                    pos += len(batch)
+                    if budget_s is not None and time.perf_counter() - t0 > budget_s:
+                        break
+    return done, time.perf_counter() - t0
+
+
+def _f64(t):
+    import numpy as np
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_prefill_rate(qr, kr, v, rows, dim_cut, threads, budget_s=None):
+    """The oracle (as it stands) on the given query rows of batch 0 of a
+    prefill, one row per task; returns (rows done, seconds, dense-equivalent
+    FLOPs of those rows)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
-
     import oracle as O
+    Hq, d = qr.shape[2], qr.shape[3]
+    rows = [int(r) for r in rows]
+    ridx = torch.tensor(rows, device=qr.device)
+    q64 = _f64(qr[0, ridx])
+    k64, v64 = _f64(kr[0]), _f64(v[0])
+    where = {r: i for i, r in enumerate(rows)}
 
-    def f64(t):
-        return t.float().cpu().numpy().astype(np.float64)
+    def one(i):
+        j = where[i]
+        O.prefill(q64[j:j + 1], k64, v64, dim_cut, rows=[i], q_is_rows=True)
+
+    done, dt = _timed_rows(one, rows, threads, budget_s)
+    flops = sum(4.0 * d * Hq * (i + 1) for i in done)
+    return np.array(done), dt, flops
+
+
+def cpu_baseline(qr, kr, v, n, Hq, d_h, G, theta, seconds, seed=11, max_rows=4096):
+    """The CPU oracle (float64 numpy, as it stands) on seeded uniform query
+    rows of the 32K prefill (the rotated inputs the GPU consumed), on every
+    host CPU available (one row per thread), and on one thread for
+    comparison; scaled to dense-equivalent TFLOP/s."""
+    import numpy as np
+    import oracle as O
 
     rng = np.random.default_rng(seed)
     rows = rng.integers(0, n, size=max_rows)
-    q64 = f64(qr[0, torch.from_numpy(rows).to(qr.device)])
-    k64 = f64(kr[0])
-    v64 = f64(v[0])
-    cut = O.group_cutoffs(theta, d_h, G)
-    dc = O.dim_cutoffs_grouped(cut, G)
-    done = 0
-    flops = 0.0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while done < max_rows and (time.perf_counter() - t0 < seconds or done < 4):
-            i = int(rows[done])
-            O.prefill(q64[done:done + 1], k64, v64, dc, rows=[i], q_is_rows=True)
-            flops += 4.0 * d_h * Hq * (i + 1)
-            done += 1
-        dt = time.perf_counter() - t0
-    done_rows = rows[:done]
+    dc = O.dim_cutoffs_grouped(O.group_cutoffs(theta, d_h, G), G)
+    threads = _oracle_threads()
+    done, dt, flops = oracle_prefill_rate(qr, kr, v, rows, dc, threads, seconds)
+    done1, dt1, flops1 = oracle_prefill_rate(qr, kr, v, rows[:64], dc, 1, seconds / 3)
     # labelled extrapolation to the whole prefill: the oracle's cost per row
     # grows with the row's causal length, so scale by sum(i + 1) over all rows
     # / over the sampled rows
-    scale = (n * (n + 1) / 2.0) / float(np.sum(done_rows + 1))
+    scale = (n * (n + 1) / 2.0) / float(np.sum(done + 1))
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s (prefill, dense-equivalent)",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%d seeded uniform query rows x %d heads of the 32K prefill "
-                  "(grouped rule, float64 numpy, 1 BLAS thread), %.1f s" % (len(done_rows), Hq, dt),
+        "sample": "%d seeded uniform query rows x %d heads of the 32K prefill (grouped rule, float64 "
+                  "numpy), one row per host thread on %d threads, %.1f s" % (len(done), Hq, threads, dt),
         "extrapolated_full_prefill_s": round(dt * scale, 1),
+        "single_thread": {"value": flops1 / dt1 / 1e12, "cores": 1,
+                          "sample": "%d of the same rows on one thread, %.1f s" % (len(done1), dt1)},
         "host_cpus_available": len(os.sched_getaffinity(0)),
     }
+
+
+# The other prefill workloads (the headline is the 32K G = 16 prefill and the
+# 16 x 32K decode): name -> (B, n, Hq, Hkv, d_h, G, theta, pos_scale, fp32 Q/K,
+# per-channel std, oracle rows (0 = all), warmups, timed launches)
+PREFILL_CONFIGS = {
+    "tiny256": (1, 256, 1, 1, 64, 16, 1e4, 1.0, True, False, 0, 3, 10),
+    "prefill4k": (1, 4096, 32, 8, 128, 16, 1e6, 1.0, False, True, 0, 3, 10),
+    "prefill32k_g32": (1, 32768, 32, 8, 128, 32, 1e6, 1.0, False, False, 256, 3, 10),
+    "prefill128k_s4": (1, 131072, 64, 8, 128, 16, 1e6, 4.0, False, False, 128, 1, 3),
+}
+
+
+# evaluation variants timed next to the default kernel of a workload
+PREFILL_VARIANTS = {}
+
+
+def _time_launches(fn, warmup, reps):
+    """warmup calls, then reps calls each bracketed by events on the launch
+    stream; returns the times in ms."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def bench_prefill_config(W, name, gen, with_oracle, extra_flags=()):
+    """One prefill workload: RoPE of the raw Q and K, then the WavePrune
+    prefill and the dense baseline, each timed as the pages time prefill
+    (warmups, then the median of the timed launches).  With with_oracle, the
+    oracle is timed on the workload's rows (all, or the sampled rows with the
+    labelled extrapolation to the whole prefill) on every host thread."""
+    import numpy as np
+    import torch
+    from rope_positional_encoding_amd import synth
+    B, n, Hq, Hkv, d, G, theta, s, fp32, chstd, orows, warm, reps = PREFILL_CONFIGS[name]
+    log("bench: %s" % name)
+    dev = torch.device("cuda:0")
+    dt_in = torch.float32 if fp32 else torch.bfloat16
+
+    def randn(shape, tid):
+        x = torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+        if chstd:
+            x *= torch.from_numpy(synth.channel_std(2, tid, d)).to(dev)
+        return x.to(dt_in)
+
+    q_raw = randn((B, n, Hq, d), synth.TID_Q)
+    k_raw = randn((B, n, Hkv, d), synth.TID_K)
+    v = randn((B, n, Hkv, d), synth.TID_V).to(torch.bfloat16)
+    qr = W.rope_apply(q_raw, theta, s)
+    kr = W.rope_apply(k_raw, theta, s)
+    o = torch.empty_like(qr)
+    cut = W.group_cutoffs(theta, d, G, s)
+    rope_ms = statistics.median(_time_launches(
+        lambda: (W.rope_apply(q_raw, theta, s, out=qr), W.rope_apply(k_raw, theta, s, out=kr)), 2, 5))
+    wp = _time_launches(lambda: W.prefill(qr, kr, v, cut, G, out=o), warm, reps)
+    dn = _time_launches(lambda: W.prefill(qr, kr, v, None, G, dense=True, out=o), warm, reps)
+    dense_f, alg_f, exe_f = prefill_flops(n, Hq, B, d, G, cut)
+    med, med_d = statistics.median(wp), statistics.median(dn)
+    avg = sum(wp) / len(wp)
+    ach = alg_f / (avg * 1e-3) / 1e12
+    res = {"shape": {"B": B, "n": n, "Hq": Hq, "Hkv": Hkv, "d_h": d, "theta": theta, "pos_scale": s, "G": G,
+                     "inputs": "fp32 Q/K" if fp32 else ("bf16, per-channel std U[0.5,2]" if chstd else "bf16")},
+           "protocol": "%d warmups, median of %d launches" % (warm, reps),
+           "ms_median": round(med, 4), "ms_min": round(min(wp), 4), "ms_max": round(max(wp), 4),
+           "dense_equiv_tflops": round(dense_f / (med * 1e-3) / 1e12, 2),
+           "algorithmic_tflops": round(alg_f / (med * 1e-3) / 1e12, 2),
+           "executed_tflops": round(exe_f / (med * 1e-3) / 1e12, 2),
+           "algorithmic_fraction_of_dense": round(alg_f / dense_f, 4),
+           "dense_ms_median": round(med_d, 4),
+           "dense_tflops": round(dense_f / (med_d * 1e-3) / 1e12, 2),
+           "dense_frac_of_peak": round(dense_f / (med_d * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "speedup_vs_dense": round(med_d / med, 4),
+           "rope_q_k_ms": round(rope_ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_ms": round(avg, 4),
+                        "kernel": "prefill_kernel<%d,%d>" % (d, G)}}
+    for fl in extra_flags:
+        # evaluation variants of the same prefill (same result, other tiling)
+        vt = _time_launches(lambda: W.prefill(qr, kr, v, cut, G, out=o, variant=fl), warm, reps)
+        vm, va = statistics.median(vt), sum(vt) / len(vt)
+        res["variant_" + fl] = {"ms_median": round(vm, 4),
+                                "algorithmic_tflops": round(alg_f / (vm * 1e-3) / 1e12, 2),
+                                "frac": round(alg_f / (va * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "time_vs_default": round(vm / med, 4)}
+    cpu = None
+    if with_oracle:
+        import oracle as O
+        dc = O.dim_cutoffs_grouped(np.array(cut), G)
+        if orows == 0:
+            rows = np.arange(n)
+        else:
+            rows = synth.sample_rows(n, orows, 7, [c + e for c in cut for e in (0, 1)])
+        threads = _oracle_threads()
+        done, dt, flops = oracle_prefill_rate(qr, kr, v, rows, dc, threads)
+        cpu = {"rows": "all %d" % n if orows == 0 else "%d sampled rows" % len(done), "seconds": round(dt, 2),
+               "threads": threads, "dense_equiv_tflops": flops / dt / 1e12 * B}
+        if orows:
+            scale = (n * (n + 1) / 2.0) / float(np.sum(done + 1))
+            cpu["extrapolated_full_prefill_s"] = round(dt * scale * B, 1)
+            cpu["extrapolation"] = "x sum(i+1) over all rows / over the sampled rows"
+    del q_raw, k_raw, v, qr, kr, o
+    torch.cuda.empty_cache()
+    return res, cpu
+
+
+def oracle_decode_rate(dq, kc, vc, L, q_pos, cut, G, threads):
+    """The oracle on every sequence of a decode (all cached keys), one
+    sequence per host thread; returns (seconds, dense KV bytes)."""
+    import numpy as np
+    import oracle as O
+    dc = O.dim_cutoffs_grouped(np.array(cut), G)
+    B = dq.shape[0]
+    q64 = _f64(dq)
+    ks = [_f64(kc[b, :L]) for b in range(B)]
+    vs = [_f64(vc[b, :L]) for b in range(B)]
+    _, dt = _timed_rows(lambda b: O.decode(q64[b], ks[b], vs[b], q_pos, L, dc), list(range(B)), threads)
+    return dt, 2.0 * 2 * B * L * kc.shape[2] * kc.shape[3]
 
 
 def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops):
@@ -337,11 +512,13 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-kcache", action="store_true", help="skip the compact K store decode line")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward line")
     ap.add_argument("--no-exact", action="store_true", help="skip the exact per-channel rule (G = 2) line")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (tiny256, prefill4k, prefill32k_g32, prefill128k_s4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (3 launches): a kernel of known "
                          "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -521,9 +698,38 @@ def main():
     if not args.no_exact:
         out["exact_rule"] = bench_exact(W, qr, kr, v, dqr[:, 0], kcs, vcs, cl, qp, ws, od, theta, n, Hq, Hkv, d,
                                         Bd, L, q_pos, med["prefill"], dmed, bwd_ms)
-    if not args.no_cpu_baseline:
+    with_oracle = not args.no_cpu_baseline
+    cpu_cfg = {}
+    if with_oracle:
         log("bench: cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(qr, kr, v, n, Hq, d, G, theta, args.cpu_seconds)
+        # the oracle on the rows the tests check, per workload: sampled rows of
+        # the 32K prefill (with the labelled extrapolation), every sequence of
+        # the decode
+        import numpy as np
+        import oracle as O
+        from rope_positional_encoding_amd import synth
+        threads = _oracle_threads()
+        rows = synth.sample_rows(n, 256, 7, [c + e for c in cut for e in (0, 1)])
+        done, dt, fl = oracle_prefill_rate(qr, kr, v, rows, O.dim_cutoffs_grouped(np.array(cut), G), threads)
+        cpu_cfg["prefill32k_g16"] = {
+            "rows": "%d sampled rows" % len(done), "seconds": round(dt, 2), "threads": threads,
+            "dense_equiv_tflops": fl / dt / 1e12,
+            "extrapolated_full_prefill_s": round(dt * (n * (n + 1) / 2.0) / float(np.sum(done + 1)), 1),
+            "extrapolation": "x sum(i+1) over all rows / over the sampled rows"}
+        ddt, kvb = oracle_decode_rate(dqr[:, 0], kc, vc, L, q_pos, cut, G, threads)
+        cpu_cfg["decode32k"] = {"rows": "all %d sequences x %d keys" % (Bd, L), "seconds": round(ddt, 2),
+                                "threads": threads, "kv_gbs_dense_equiv": kvb / ddt / 1e9}
+    if not args.no_configs:
+        out["configs"] = {}
+        for name in PREFILL_CONFIGS:
+            res, c = bench_prefill_config(W, name, gen, with_oracle,
+                                          extra_flags=PREFILL_VARIANTS.get(name, ()))
+            out["configs"][name] = res
+            if c is not None:
+                cpu_cfg[name] = c
+    if with_oracle:
+        out["cpu_baseline"]["per_config"] = cpu_cfg
     print(json.dumps(out), flush=True)
 
 
