@@ -158,9 +158,10 @@ wp_status wp_rope_apply(const void* x, int32_t x_dtype, void* y,
  * counters[3*(d_h/G)] the number of visited tiles.  Counts are added; the
  * caller zeroes the buffer.  May be NULL otherwise.
  * n >= 1, B >= 1, Hkv >= 1, Hq % Hkv == 0.  The k and v token strides must be
- * >= d_h, and (n-1) * token_stride + d_h elements of one sequence must span
- * less than 2^31 bytes (K/V are read through 32-bit-addressed buffer
- * resources); otherwise WP_ERR_SHAPE.
+ * >= d_h and below 2^30 elements, and one 64-token tile, 63 * token_stride +
+ * d_h elements, must span less than 2^31 bytes (K/V tiles are read through
+ * 32-bit-addressed buffer resources based at each tile; a sequence may span
+ * any number of bytes); otherwise WP_ERR_SHAPE.
  */
 wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                      int32_t B, int32_t n, int32_t Hq, int32_t Hkv, int32_t d_h,
@@ -184,8 +185,8 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
  * the forward's natural-log LSE [B][Hq][n]; dq [B, n, Hq, d_h], dk and dv
  * [B, n, Hkv, d_h] bf16, written (not accumulated).  strides[24] = {q, k, v,
  * o, dout, dq, dk, dv} x {batch, token, head} in elements; the q, k, v and
- * dout token strides must be >= d_h and one sequence of each must span less
- * than 2^31 bytes.  cutoffs and G as in wp_prefill; flags: WP_FLAG_DENSE or
+ * dout token strides must be >= d_h and one 64-token tile of each must span
+ * less than 2^31 bytes (as in wp_prefill).  cutoffs and G as in wp_prefill; flags: WP_FLAG_DENSE or
  * 0.  workspace: device memory of at least
  * wp_prefill_backward_workspace_size(B, n, Hq) bytes, 256-byte aligned (two
  * floats per query row: its LSE in base 2 and its row sum Dsum).
@@ -223,8 +224,10 @@ size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq);
  * 256-byte aligned, used for the per-split partial results.
  * counters (WP_FLAG_COUNT): device int64[3*(d_h/G)+1], as in wp_prefill but
  * counted per (sequence, kv head, key block).
- * The cache token strides must be >= d_h and one sequence of the cache must
- * span less than 2^31 bytes (WP_ERR_SHAPE otherwise).
+ * The cache token strides must be >= d_h and one 32-token block of the cache,
+ * 31 * token_stride + d_h elements, must span less than 2^31 bytes (each
+ * block is read through its own 32-bit-addressed buffer resources; a cache
+ * may span any number of bytes); WP_ERR_SHAPE otherwise.
  */
 wp_status wp_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                     const int32_t* cache_len, const int32_t* q_pos,

@@ -61,6 +61,13 @@ wp_status check_strides(const int64_t* st, int count) {
   return WP_OK;
 }
 
+// Rows of K, V (and in the backward Q, dO) are read through 32-bit buffer
+// resources that span one tile of `rows` tokens: the tile's byte span, and
+// the byte stride itself, must stay below 2^31.
+bool tile_span_ok(int64_t token_stride, int32_t d_h, int rows) {
+  return token_stride * 2 < 2147483647LL && (int64_t)(rows - 1) * token_stride * 2 + 2 * d_h < 2147483647LL;
+}
+
 // Classes of one tile with causal distances [lD, rD]: skip groups
 // [0, splitL), partial [splitL, splitR), full [splitR, ng).
 inline void add_tile(const int32_t* cut, int ng, int64_t lD, int64_t rD, int64_t* counts) {
@@ -262,13 +269,13 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
   if (counters && (reinterpret_cast<uintptr_t>(counters) & 7u))
     return fail(WP_ERR_ALIGN, "counters must be 8-byte aligned");
   if (wp_status s = check_strides(strides, 12)) return s;
-  // K/V rows are fetched through buffer resources: rows must not overlap and
-  // one sequence's rows must span less than 2^31 bytes
+  // K/V rows are fetched through buffer resources, one per 64-key tile: rows
+  // must not overlap and one tile's rows must span less than 2^31 bytes (any
+  // sequence length)
   if (strides[4] < d_h || strides[7] < d_h)
     return fail(WP_ERR_SHAPE, "k/v token strides must be >= d_h");
-  if ((int64_t)(n - 1) * strides[4] * 2 + 2 * d_h >= 2147483647LL ||
-      (int64_t)(n - 1) * strides[7] * 2 + 2 * d_h >= 2147483647LL)
-    return fail(WP_ERR_SHAPE, "one sequence of K or V spans 2^31 bytes or more");
+  if (!tile_span_ok(strides[4], d_h, 64) || !tile_span_ok(strides[7], d_h, 64))
+    return fail(WP_ERR_SHAPE, "a 64-token tile of K or V spans 2^31 bytes or more (token stride too large)");
   const int ng = d_h / G;
   wp::PrefillArgs a;
   memset(&a, 0, sizeof(a));
@@ -399,9 +406,8 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
   if (wp_status s = check_strides(st10, 10)) return s;
   if ((!compact && st10[3] < d_h) || st10[6] < d_h)
     return fail(WP_ERR_SHAPE, "k/v cache token strides must be >= d_h");
-  if ((!compact && (int64_t)(Lmax - 1) * st10[3] * 2 + 2 * d_h >= 2147483647LL) ||
-      (int64_t)(Lmax - 1) * st10[6] * 2 + 2 * d_h >= 2147483647LL)
-    return fail(WP_ERR_SHAPE, "one sequence of the K or V cache spans 2^31 bytes or more");
+  if ((!compact && !tile_span_ok(st10[3], d_h, 32)) || !tile_span_ok(st10[6], d_h, 32))
+    return fail(WP_ERR_SHAPE, "a 32-token block of the K or V cache spans 2^31 bytes or more (token stride too large)");
   const size_t need = wp_decode_workspace_size(B, Lmax, Hq, Hkv, d_h, num_splits);
   if (workspace_bytes < need)
     return fail(WP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
@@ -524,12 +530,12 @@ wp_status wp_prefill_backward(const void* q, const void* k, const void* v, const
     return fail(WP_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (wp_status s = check_strides(strides, 24)) return s;
   // Q, dO (dK/dV kernel) and K, V (dQ kernel) rows are fetched through
-  // buffer resources: token strides >= d_h, one sequence < 2^31 bytes
+  // buffer resources: token strides >= d_h, one 64-token tile < 2^31 bytes
   const int tok[4] = {1, 4, 7, 13};
   for (int t : tok) {
     if (strides[t] < d_h) return fail(WP_ERR_SHAPE, "q, k, v, dO token strides must be >= d_h");
-    if ((int64_t)(n - 1) * strides[t] * 2 + 2 * d_h >= 2147483647LL)
-      return fail(WP_ERR_SHAPE, "one sequence of q, k, v or dO spans 2^31 bytes or more");
+    if (!tile_span_ok(strides[t], d_h, 64))
+      return fail(WP_ERR_SHAPE, "a 64-token tile of q, k, v or dO spans 2^31 bytes or more (token stride too large)");
   }
   const size_t need = wp_prefill_backward_workspace_size(B, n, Hq);
   if (workspace_bytes < need)

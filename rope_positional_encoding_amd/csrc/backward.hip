@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   auto load_tile = [&](int hr, int ti, unsigned char* dst, float* ldst) {
     const int h = kvh * a.r + hr;
     const int i0 = (t0 + ti) * 32;
-    const int rows = n - i0;
+    const int rows = min(32, n - i0);         // the tile's own rows: 32-bit offsets
     const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(
         a.q + (int64_t)b * a.qs_b + (int64_t)i0 * a.qs_t + (int64_t)h * a.qs_h, (rows - 1) * qrow_b + 2 * D);
     const __amdgpu_buffer_rsrc_t grs = uniform_rsrc(
@@ -686,7 +686,7 @@ __global__ __launch_bounds__(kDqThreads, G == 2 ? 1 : 2) void bwd_dq_kernel(Back
     voff[i] = row * vrow_b + (pc ^ ((row / KRB) & (CPR - 1))) * 16;
   }
   auto load_tile = [&](int j0, int st) {
-    const int rows = n - j0;
+    const int rows = min(64, n - j0);          // the tile's own rows: 32-bit offsets
     const __amdgpu_buffer_rsrc_t krs =
         uniform_rsrc(kbase + (int64_t)j0 * a.ks_t, (rows - 1) * krow_b + 2 * D);
     const __amdgpu_buffer_rsrc_t vrs =

@@ -98,15 +98,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       qr[p] = (n16 < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
   }
 
-  // K / V of this (sequence, kv head) through raw buffer resources that end
-  // after row L-1: rows past the cache length read as zero, and a lane whose
-  // 8 dims belong to a skipped group gets an out-of-range offset, so it
-  // fetches nothing and reads zero -- no branches around the loads.
+  // K / V of this (sequence, kv head) through raw buffer resources.  For the
+  // full cache each 32-key block gets its own resources, from its first key
+  // to min(L, block end) - 1, so offsets stay within one block (32-bit,
+  // whatever the cache length): rows past the cache length read as zero, and
+  // a lane whose 8 dims belong to a skipped group gets an out-of-range
+  // offset, so it fetches nothing and reads zero -- no branches around the
+  // loads.  The compact store is one resource per (sequence, kv head).
   const int krow_b = (int)(a.ks_t * 2);
   const int vrow_b = (int)(a.vs_t * 2);
-  const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(
-      a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h,
-      COMPACT ? 2 * a.kstore_elems : (L > 0 ? (L - 1) * krow_b + 2 * D : 0));
+  const bf16* kseq = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+  const bf16* vseq = a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h;
+  const __amdgpu_buffer_rsrc_t kstore = uniform_rsrc(kseq, COMPACT ? 2 * a.kstore_elems : 0);
   // compact store: ring size, its reciprocal and the ring's byte offset for
   // the group this lane reads in QK step p.  The kernel arguments are read
   // with uniform indices only (a lane-dependent index would turn them into
@@ -124,8 +127,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       rcap_p[p] = 1.0f / (float)kcap_p[p];
     }
   }
-  const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(
-      a.v + (int64_t)b * a.vs_b + (int64_t)kvh * a.vs_h, L > 0 ? (L - 1) * vrow_b + 2 * D : 0);
   constexpr int kOut = 0x7ffffff0;    // any offset >= the resource size
 
   bf16* sv = sV[wave];
@@ -195,10 +196,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   auto load_block = [&](Regs& R, int jb) {
     int sL, sR;
     classify(jb, sL, sR);
+    const int rows = min(32, L - jb);          // >= 1
+    const __amdgpu_buffer_rsrc_t krs =
+        COMPACT ? kstore : uniform_rsrc(kseq + (int64_t)jb * a.ks_t, (rows - 1) * krow_b + 2 * D);
+    const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(vseq + (int64_t)jb * a.vs_t, (rows - 1) * vrow_b + 2 * D);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int j = jb + 16 * blk + n16;
-      const int row = j * krow_b;
+      const int row = (16 * blk + n16) * krow_b;     // within the block
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int dim = 32 * p + 8 * q4;
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       const int dc = (lane >> 3) + 8 * it;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        R.v[it][e] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (jb + 4 * kq + e) * vrow_b + dc * 16, 0, 0);
+        R.v[it][e] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (4 * kq + e) * vrow_b + dc * 16, 0, 0);
     }
   };
 

@@ -30,6 +30,8 @@
 //    classes.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ...
 //    lds: no register staging, rows past the sequence end arrive as zeros).
+//    The buffer resources of a tile start at its first key and end after its
+//    last, so every offset is within one tile (32-bit, whatever the length).
 //    Both are stored row-major with an XOR swizzle of their 16-byte chunks.
 //    LDS has 64 banks of 4 bytes (one 256-byte bank row) and serves 16 lanes
 //    of a 16-byte read at a time, so K is swizzled by the index of the row's
@@ -130,8 +132,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     koff[i] = row * krow_b + (pc ^ ((row / KRB) & (CPR - 1))) * 16;
     voff[i] = row * vrow_b + (pc ^ ((row & 3) * VX)) * 16;
   }
+  // each tile's buffer resources start at its first key and span its own
+  // rows (at most 64), so offsets stay 32-bit whatever the sequence length
   auto load_tile = [&](int j0, int stage) {
-    const int rows = n - j0;                                  // >= 1
+    const int rows = min(kTileKeys, n - j0);                  // >= 1
     const __amdgpu_buffer_rsrc_t kr =
         uniform_rsrc(kbase + (int64_t)j0 * a.ks_t, (rows - 1) * krow_b + 2 * D);
     const __amdgpu_buffer_rsrc_t vr =

@@ -257,8 +257,14 @@ def test_prefill_validation_codes():
     st[4] = 64                                           # k token stride < d_h
     assert _prefill(strides=st) == -2
     st = _strides(12)
-    st[7] = 1 << 24                                      # one V sequence > 2 GiB
+    st[7] = 1 << 25                                      # one 64-token V tile > 2 GiB
     assert _prefill(strides=st, n=200) == -2
+    # 64 KB per token: a 4 GiB sequence at n = 65536 passes the span checks
+    # (a tile spans 4 MB) and stops at the cutoff table, checked after them
+    st = _strides(12)
+    st[4] = st[7] = 1 << 15
+    assert _prefill(strides=st, n=1 << 16, cut=(ctypes.c_int32 * 8)(9, 8, 7, 6, 5, 4, 3, 2)) == -6
+    assert "non-decreasing" in W.lib().wp_last_error().decode()
 
 
 def _decode(**kw):
@@ -269,14 +275,21 @@ def _decode(**kw):
     return W.lib().wp_decode(*args.values())
 
 
-def test_decode_largest_cache_span():
-    # 2^20 keys at a 2 KB token stride end 2 KB short of 2^31 bytes and pass
-    # validation (stopped here by the small workspace); one key more is
-    # rejected (the K/V buffer resources address 32 bits)
+def test_decode_cache_span_limits():
+    # every 32-key block is read through its own 32-bit buffer resources, so
+    # the cache length is not limited by the byte span: 2^20 + 1 and 2^22 keys
+    # at a 2 KB token stride (1 M tokens x 8 kv heads x 128 dims is 2 GiB of K
+    # per sequence) pass validation (stopped here by the small workspace);
+    # a token stride whose 32-token block spans 2^31 bytes is rejected
     st = _strides(10)
     st[3] = st[6] = 8 * 128                              # k_t, v_t in elements
-    assert _decode(B=1, Lmax=1 << 20, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -5
-    assert _decode(B=1, Lmax=(1 << 20) + 1, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -2
+    for L in (1 << 20, (1 << 20) + 1, 1 << 22):
+        assert _decode(B=1, Lmax=L, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -5
+    st[3] = 1 << 26                                      # 128 MB per token: a block spans 4 GB
+    assert _decode(B=1, Lmax=100, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -2
+    st = _strides(10)
+    st[6] = (1 << 30) + 8                                # byte stride past 2^31
+    assert _decode(B=1, Lmax=1, Hq=8, Hkv=2, strides=st, ws_bytes=16) == -2
 
 
 def test_decode_validation_codes():

@@ -167,14 +167,15 @@ def test_backward_strided_views():
     assert torch.count_nonzero(grad[:, :, 0]) == 0 and torch.count_nonzero(grad[:, :, 1 + H]) == 0
 
 
-def test_backward_largest_span():
-    """q, k, v and dO as head views at a 512 KB token stride, 4096 tokens:
-    every input sequence ends just short of 2^31 bytes from its first row,
-    the most the 32-bit buffer addressing takes.  dQ at sampled rows and the
-    last 48 rows, dK and dV at the last 48 keys, against the oracle."""
-    n, Hq, Hkv, Hall, d, G, theta = 4096, 4, 1, 2048, 128, 16, 1e4
+def test_backward_past_2gib():
+    """q, k, v and dO as head views at a 512 KB token stride, 6144 tokens:
+    every input sequence reaches 3 GiB past its first row, past what one
+    32-bit buffer resource spans (tiles are read through their own).  dQ at
+    sampled rows and the last 48 rows, dK and dV at the last 48 keys, against
+    the oracle."""
+    n, Hq, Hkv, Hall, d, G, theta = 6144, 4, 1, 2048, 128, 16, 1e4
     tail = 48
-    say("backward largest span: n=%d token stride %d bytes" % (n, Hall * d * 2))
+    say("backward past 2 GiB: n=%d token stride %d bytes" % (n, Hall * d * 2))
     x = [synth.normal_bits(97, t, n, (h, d)) for t, h in ((0, Hq), (1, Hkv), (2, Hkv), (3, Hq))]
     views = []
     bigs = []
@@ -184,7 +185,7 @@ def test_backward_largest_span():
         bigs.append(big)
         views.append(big[:, :, Hall - h:])
     qt, kt, vt, gt = views
-    assert (n - 1) * Hall * d * 2 + 2 * d * Hq < 2 ** 31 - 1
+    assert (n - 1) * Hall * d * 2 > 3 * 2 ** 30 - 2 ** 20
     cut = W.group_cutoffs(theta, d, G)
     o, lse = W.prefill(qt, kt, vt, cut, G, return_lse=True)
     dq, dk, dv = W.prefill_backward(qt, kt, vt, o, gt, lse, cut, G)

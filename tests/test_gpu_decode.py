@@ -219,30 +219,30 @@ def test_decode_wide_gqa(B, Lmax, Hq, Hkv, d, G, theta, lens, splits):
     assert np.array_equal(cnt.cpu().numpy(), _expected(lens, lens, d, G, cut, Hkv))
 
 
-def test_decode_largest_cache_span():
-    """The largest cache the 32-bit buffer addressing takes: one sequence of
-    2^20 keys whose token stride is 2 KB (the cache holds 8 kv heads; heads 0
-    and 1 are used through a strided view), so the last key sits 2 KB short
-    of 2 GiB from the sequence start.  Against the oracle, counters
-    bit-exact (one token more is rejected by validation: tests/test_abi.py)."""
-    L, Hq, Hkv, Hall, d, G, theta = 1 << 20, 8, 2, 8, 128, 16, 1e6
-    say("decode largest span: L=%d token stride %d bytes" % (L, Hall * d * 2))
+def test_decode_cache_past_2gib():
+    """A cache longer than one 32-bit buffer resource could span: one
+    sequence of 3 x 2^19 keys (1.5 M) whose token stride is 2 KB (the cache
+    holds 8 kv heads; the last one is used through a strided view), so its
+    keys reach 3 GiB past the sequence start.  Every 32-key block is read
+    through its own resources.  Against the oracle, counters bit-exact."""
+    L, Hq, Hkv, Hall, d, G, theta = 3 << 19, 4, 1, 8, 128, 16, 1e6
+    say("decode past 2 GiB: L=%d token stride %d bytes, span %.2f GiB" % (L, Hall * d * 2, L * Hall * d * 2 / 2 ** 30))
     q = synth.normal_bits(83, 0, 1, (Hq, d))
     kc = synth.normal_bits(83, 1, L, (Hkv, d))
     vc = synth.normal_bits(83, 2, L, (Hkv, d))
     kbig = torch.zeros((1, L, Hall, d), dtype=torch.bfloat16, device=dev())
     vbig = torch.zeros((1, L, Hall, d), dtype=torch.bfloat16, device=dev())
-    kbig[:, :, :Hkv] = bits_to_dev(kc, (1, L, Hkv, d))
-    vbig[:, :, :Hkv] = bits_to_dev(vc, (1, L, Hkv, d))
+    kbig[:, :, Hall - Hkv:] = bits_to_dev(kc, (1, L, Hkv, d))
+    vbig[:, :, Hall - Hkv:] = bits_to_dev(vc, (1, L, Hkv, d))
     cut = W.group_cutoffs(theta, d, G)
     qt = bits_to_dev(q, (1, Hq, d))
     cl = torch.tensor([L], dtype=torch.int32, device=dev())
     qp = torch.tensor([L], dtype=torch.int32, device=dev())
     cnt = torch.zeros(3 * (d // G) + 1, dtype=torch.int64, device=dev())
-    o = W.decode(qt, kbig[:, :, :Hkv], vbig[:, :, :Hkv], cl, qp, cut, G, counters=cnt)
+    o = W.decode(qt, kbig[:, :, Hall - Hkv:], vbig[:, :, Hall - Hkv:], cl, qp, cut, G, counters=cnt)
     torch.cuda.synchronize()
     got = bf16_to_np(o)[0]
     del kbig, vbig
     ref = O.decode(to_f64(q[0]), to_f64(kc), to_f64(vc), L, L, O.dim_cutoffs_grouped(np.array(cut), G))
-    compare(got, ref, "decode L=2^20")
+    compare(got, ref, "decode L=1.5M (3 GiB span)")
     assert np.array_equal(cnt.cpu().numpy(), _expected([L], [L], d, G, cut, Hkv))

@@ -196,14 +196,14 @@ def test_workload_prefill128k_scaled():
     _run_workload("prefill128k_s4")
 
 
-def test_prefill_largest_kv_span():
-    """K and V at the largest span the 32-bit buffer addressing takes: 4096
+def test_prefill_kv_past_2gib():
+    """K and V sequences past what one 32-bit buffer resource spans: 6144
     tokens at a 512 KB token stride (views of one head out of 2048), so the
-    last key of the sequence ends 0.5 MB short of 2^31 bytes.  Sampled rows
-    against the oracle, counters bit-exact."""
-    n, Hq, Hkv, Hall, d, G, theta = 4096, 4, 1, 2048, 128, 16, 1e4
-    say("prefill largest span: n=%d token stride %d bytes" % (n, Hall * d * 2))
-    assert (n - 1) * Hall * d * 2 + 2 * d < 2 ** 31 - 1
+    last key sits 3 GiB past the first (each 64-key tile is read through its
+    own resources).  Sampled rows against the oracle, counters bit-exact."""
+    n, Hq, Hkv, Hall, d, G, theta = 6144, 4, 1, 2048, 128, 16, 1e4
+    say("prefill past 2 GiB: n=%d token stride %d bytes" % (n, Hall * d * 2))
+    assert (n - 1) * Hall * d * 2 > 3 * 2 ** 30 - 2 ** 20
     q = synth.normal_bits(91, 0, n, (Hq, d))
     k = synth.normal_bits(91, 1, n, (Hkv, d))
     v = synth.normal_bits(91, 2, n, (Hkv, d))
