@@ -231,7 +231,7 @@ PREFILL_CONFIGS = {
 
 
 # evaluation variants timed next to the default kernel of a workload
-PREFILL_VARIANTS = {}
+PREFILL_VARIANTS = {"prefill32k_g32": ("mfma16x16x32",)}
 
 
 def _time_launches(fn, warmup, reps):
@@ -308,7 +308,9 @@ def bench_prefill_config(W, name, gen, with_oracle, extra_flags=()):
         # evaluation variants of the same prefill (same result, other tiling)
         vt = _time_launches(lambda: W.prefill(qr, kr, v, cut, G, out=o, variant=fl), warm, reps)
         vm, va = statistics.median(vt), sum(vt) / len(vt)
-        res["variant_" + fl] = {"ms_median": round(vm, 4),
+        vd = _time_launches(lambda: W.prefill(qr, kr, v, None, G, dense=True, out=o, variant=fl), warm, reps)
+        res["variant_" + fl] = {"ms_median": round(vm, 4), "dense_ms_median": round(statistics.median(vd), 4),
+                                "speedup_vs_dense": round(statistics.median(vd) / vm, 4),
                                 "algorithmic_tflops": round(alg_f / (vm * 1e-3) / 1e12, 2),
                                 "frac": round(alg_f / (va * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                 "time_vs_default": round(vm / med, 4)}

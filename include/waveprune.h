@@ -64,6 +64,10 @@ typedef int32_t wp_status;
 #define WP_FLAG_DENSE 1u  /* ignore the cutoffs: every group is full (plain RoPE
                              attention; the in-house dense baseline) */
 #define WP_FLAG_COUNT 2u  /* add tile-class counts into `counters` */
+#define WP_FLAG_MFMA16 4u /* wp_prefill only, d_h = 128 and G = 32: run the
+                             v_mfma_f32_16x16x32_bf16 kernel (one MFMA step per
+                             32-dim group) instead of the 32x32x16 one; same
+                             tiles, same results up to summation order */
 
 /* Largest cutoff value: a group with this cutoff is never pruned. */
 #define WP_NEVER_PRUNE 2147483647

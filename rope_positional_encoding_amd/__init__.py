@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libwaveprune.so")
 
 FLAG_DENSE = 1
 FLAG_COUNT = 2
+FLAG_MFMA16 = 4
 NEVER_PRUNE = 2 ** 31 - 1
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
@@ -225,10 +226,13 @@ def rope_apply(x: torch.Tensor, theta: float, pos_scale: float = 1.0,
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cutoffs: Optional[Sequence[int]],
             G: int, dense: bool = False, return_lse: bool = False,
             counters: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None):
+            lse: Optional[torch.Tensor] = None, variant: Optional[str] = None):
     """Causal WavePrune attention.  q [B, n, Hq, d_h], k/v [B, n, Hkv, d_h]
     (bf16, q/k rotated).  counters: device int64 [3*(d_h/G)+1] to add tile
-    counts into (enables WP_FLAG_COUNT)."""
+    counts into (enables WP_FLAG_COUNT).  variant "mfma16x16x32" selects the
+    v_mfma_f32_16x16x32_bf16 kernel (d_h = 128, G = 32: WP_FLAG_MFMA16)."""
+    if variant not in (None, "mfma16x16x32"):
+        raise ValueError("unknown prefill variant %r" % (variant,))
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16, 4)
     B, n, Hq, d = q.shape
@@ -240,7 +244,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cutoffs: Optional
     _need(out, "out", torch.bfloat16, 4)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
-    flags = (FLAG_DENSE if dense else 0) | (FLAG_COUNT if counters is not None else 0)
+    flags = ((FLAG_DENSE if dense else 0) | (FLAG_COUNT if counters is not None else 0)
+             | (FLAG_MFMA16 if variant == "mfma16x16x32" else 0))
     cut = None if cutoffs is None else _cut(cutoffs, d, G)
     strides = list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3]) + list(out.stride()[:3])
     _check(lib().wp_prefill(

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwaveprune.so")
 CHECK = os.path.join(ROOT, "tests", "c_abi_check")
-SOURCES = ["api.hip", "rope.hip", "prefill.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "rope.hip", "prefill.hip", "prefill16.hip", "decode.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed FP32 VALU forms are switched off for all device code.  IEEE mode is

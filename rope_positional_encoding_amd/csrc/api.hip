@@ -255,12 +255,16 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
                      const int32_t* cutoffs, int32_t G, uint32_t flags, int64_t* counters,
                      void* stream) {
   if (!q || !k || !v || !o || !strides) return fail(WP_ERR_NULL, "q, k, v, o or strides is NULL");
-  if (flags & ~(WP_FLAG_DENSE | WP_FLAG_COUNT)) return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(WP_FLAG_DENSE | WP_FLAG_COUNT | WP_FLAG_MFMA16))
+    return fail(WP_ERR_ARG, "unknown flags 0x%x", flags);
   const bool dense = flags & WP_FLAG_DENSE;
   const bool count = flags & WP_FLAG_COUNT;
+  const bool mfma16 = flags & WP_FLAG_MFMA16;
   if (!dense && !cutoffs) return fail(WP_ERR_NULL, "cutoffs is NULL (and WP_FLAG_DENSE not set)");
   if (count && !counters) return fail(WP_ERR_NULL, "counters is NULL with WP_FLAG_COUNT");
   if (!supported_shape(d_h, G)) return fail(WP_ERR_UNSUPPORTED, "d_h=%d G=%d unsupported", d_h, G);
+  if (mfma16 && !(d_h == 128 && G == 32))
+    return fail(WP_ERR_UNSUPPORTED, "WP_FLAG_MFMA16 takes d_h = 128 and G = 32 (d_h=%d G=%d)", d_h, G);
   if (B < 1 || n < 1 || Hq < 1 || Hkv < 1) return fail(WP_ERR_SHAPE, "B, n, Hq, Hkv must be >= 1");
   if (Hq % Hkv) return fail(WP_ERR_SHAPE, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -305,7 +309,8 @@ wp_status wp_prefill(const void* q, const void* k, const void* v, void* o, float
   // is the smallest workgroup, so this bounds every grid
   const long long max_blocks = (long long)B * Hkv * a.HG * ((n + 31) / 32);
   if (max_blocks > 2147483647LL) return fail(WP_ERR_SHAPE, "grid too large");
-  hipError_t e = wp::launch_prefill(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = mfma16 ? wp::launch_prefill16(a, count, reinterpret_cast<hipStream_t>(stream))
+                        : wp::launch_prefill(a, d_h, G, count, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }

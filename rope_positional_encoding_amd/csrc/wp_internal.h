@@ -135,6 +135,8 @@ struct BackwardArgs {
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipStream_t s);
+// the v_mfma_f32_16x16x32_bf16 prefill (d_h = 128, G = 32)
+hipError_t launch_prefill16(const PrefillArgs& a, bool count, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t s);
 hipError_t launch_kcache_append(const KAppendArgs& a, hipStream_t s);
 

@@ -106,6 +106,8 @@ static void prefill_and_backward() {
                         (int64_t*)cnt.p, nullptr) == WP_OK);
       EXPECT(wp_prefill(q.p, k.p, v.p, o.p, nullptr, B, n, Hq, Hkv, d, st, nullptr, G, WP_FLAG_DENSE, nullptr,
                         nullptr) == WP_OK);
+      EXPECT(wp_prefill(q.p, k.p, v.p, o.p, nullptr, B, n, Hq, Hkv, d, st, cut.data(), G, WP_FLAG_MFMA16, nullptr,
+                        nullptr) == ((d == 128 && G == 32) ? WP_OK : WP_ERR_UNSUPPORTED));
       // packed QKV projection output [B, n, Hq + 2 Hkv, d]
       const int Ht = Hq + 2 * Hkv;
       Buf qkv(2 * (size_t)B * n * Ht * d);

@@ -70,6 +70,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_h, int G, bool count, hipS
   return hipSuccess;
 }
 
+hipError_t launch_prefill16(const PrefillArgs& a, bool count, hipStream_t s) {
+  return launch_prefill(a, 128, 32, count, s);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t) {
   if (a.r < 1 || a.r > 16 || a.S < 1) return hipErrorInvalidValue;
   for (int b = 0; b < a.B; ++b) {

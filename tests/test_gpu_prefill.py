@@ -72,6 +72,54 @@ def test_prefill_small_all_rows(B, n, Hq, Hkv, d, G, theta, s, dense):
     assert np.array_equal(cnt.cpu().numpy(), exp), (cnt.cpu().numpy(), exp)
 
 
+# the v_mfma_f32_16x16x32_bf16 kernel (d_h 128, G 32): the same checks on
+# every row, ragged tails, GQA ratios 1/2/3/4/8/32, small thetas (skip,
+# partial, full and fully pruned keys), dense
+SMALL_MFMA16 = [
+    # B, n, Hq, Hkv, theta, s
+    (1, 1, 1, 1, 1e4, 1.0),
+    (2, 100, 4, 2, 30.0, 1.0),
+    (1, 777, 3, 1, 1e3, 1.0),
+    (1, 1000, 8, 1, 300.0, 1.0),
+    (1, 513, 16, 2, 1e6, 4.0),
+    (3, 161, 8, 2, 100.0, 1.0),
+    (1, 500, 32, 1, 1e4, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,n,Hq,Hkv,theta,s", SMALL_MFMA16)
+@pytest.mark.parametrize("dense", [False, True])
+def test_prefill_mfma16_all_rows(B, n, Hq, Hkv, theta, s, dense):
+    d, G = 128, 32
+    say("prefill 16x16x32 B=%d n=%d Hq=%d Hkv=%d theta=%g s=%g dense=%s" % (B, n, Hq, Hkv, theta, s, dense))
+    seed = 1500 + n + Hq
+    q = synth.normal_bits(seed, 0, B * n, (Hq, d))
+    k = synth.normal_bits(seed, 1, B * n, (Hkv, d))
+    v = synth.normal_bits(seed, 2, B * n, (Hkv, d))
+    cut = [int(c) for c in O.group_cutoffs(theta, d, G, s)]
+    qt, kt, vt = (bits_to_dev(x, (B, n, x.shape[1], d)) for x in (q, k, v))
+    cnt = _counters(d, G)
+    o = torch.full((B, n, Hq, d), float("nan"), dtype=torch.bfloat16, device=dev())
+    o, lse = W.prefill(qt, kt, vt, None if dense else cut, G, dense=dense, return_lse=True,
+                       counters=cnt, out=o, variant="mfma16x16x32")
+    o32 = W.prefill(qt, kt, vt, None if dense else cut, G, dense=dense)
+    torch.cuda.synchronize()
+    got = bf16_to_np(o).reshape(B, n, Hq, d)
+    got_lse = lse.cpu().numpy()
+    dim_cut = O.dim_cutoffs_dense(d) if dense else O.dim_cutoffs_grouped(np.array(cut), G)
+    for b in range(B):
+        sl = slice(b * n, (b + 1) * n)
+        ref, ref_lse = O.prefill(to_f64(q[sl]), to_f64(k[sl]), to_f64(v[sl]), dim_cut, return_lse=True)
+        compare(got[b], ref, "O b=%d" % b)
+        compare(got_lse[b].T, ref_lse, "LSE b=%d" % b)
+    exp = _expected_counts(n, d, G, [O.NEVER] * (d // G) if dense else cut, B * Hq)
+    assert np.array_equal(cnt.cpu().numpy(), exp), (cnt.cpu().numpy(), exp)
+    # the two MFMA shapes differ only in summation order
+    diff = (o.float() - o32.float()).abs().max().item()
+    say("  vs the 32x32x16 kernel: max-abs %.3e" % diff)
+    assert diff <= 2e-2
+
+
 def test_prefill_deterministic_and_strided():
     B, n, Hq, Hkv, d, G = 1, 700, 8, 2, 128, 16
     q = synth.normal_bits(5, 0, B * n, (Hq, d))
@@ -95,7 +143,7 @@ def test_prefill_deterministic_and_strided():
 # the workloads: raw inputs -> wp_rope_apply -> wp_prefill, oracle from the raw
 # inputs (float64 RoPE, grouped rule)
 # --------------------------------------------------------------------------
-def _run_workload(name, nrows_override=None, sep_rows=0, e2e_rows=None):
+def _run_workload(name, nrows_override=None, sep_rows=0, e2e_rows=None, variant=None):
     """Counters over the whole grid; O on the oracle's rows (nrows_override
     or the workload's own count, 0 = every row) against the bf16-in oracle;
     the end-to-end comparison against float64 RoPE on those rows, or on
@@ -121,7 +169,7 @@ def _run_workload(name, nrows_override=None, sep_rows=0, e2e_rows=None):
         kr = W.rope_apply(kd, w.theta, w.pos_scale)
         del qd, kd
         cnt = _counters(w.d_h, w.G)
-        o = W.prefill(qr, kr, vd, cut, w.G, counters=cnt)
+        o = W.prefill(qr, kr, vd, cut, w.G, counters=cnt, variant=variant)
         torch.cuda.synchronize()
     exp = _expected_counts(w.n, w.d_h, w.G, cut, w.B * w.Hq)
     got_cnt = cnt.cpu().numpy()
@@ -186,6 +234,10 @@ def test_workload_prefill4k():
 @pytest.mark.parametrize("name", ["prefill32k_g16", "prefill32k_g32"])
 def test_workload_prefill32k(name):
     _run_workload(name, sep_rows=16)
+
+
+def test_workload_prefill32k_g32_mfma16():
+    _run_workload("prefill32k_g32", variant="mfma16x16x32")
 
 
 def test_workload_prefill32k_exact():
