@@ -144,9 +144,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   __shared__ unsigned int s_hist[(COUNT && FINE) ? 2 * (NG + 1) : 1];
   // Fine groups: the cutoff table in LDS, and split points carried from
   // block to block (a wave meets its key blocks in ascending order, so the
-  // distances and the split points only decrease).
+  // distances and the split points only decrease).  cL / cR hold the cutoff
+  // of group fL - 1 / fR - 1 in scalar registers, so a block whose split
+  // points do not move reads no LDS.
   __shared__ int s_cut[FINE ? NG : 1];
   int fL = NG, fR = NG;
+  int cL = 0, cR = 0;
   if (COUNT) {
 #pragma unroll
     for (int g = 0; g < CNG; ++g) cnt[g][0] = cnt[g][1] = cnt[g][2] = 0;
@@ -157,6 +160,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   if constexpr (FINE) {
     if (tid < NG) s_cut[tid] = a.cut[tid];
     __syncthreads();
+    cL = cR = __builtin_amdgcn_readfirstlane(s_cut[NG - 1]);
   }
   const float sl2 = a.scale_log2;
 
@@ -169,16 +173,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   // [sL, sR), full [sR, NG)
   auto classify = [&](int jb, int& sL, int& sR) {
     const int jb1 = min(L, jb + 32) - 1;
-    const int lD = qp - jb1;
-    const int rD = qp - jb;
+    const int lD = __builtin_amdgcn_readfirstlane(qp - jb1);   // wave-uniform
+    const int rD = __builtin_amdgcn_readfirstlane(qp - jb);
     if constexpr (FINE) {
       // idempotent for one block, so the load and the compute of a block
       // may both call it
       auto cut_at = [&](int g) { return __builtin_amdgcn_readfirstlane(s_cut[g]); };
-      while (fL > 0 && cut_at(fL - 1) >= lD) --fL;
-      while (fR > 0 && cut_at(fR - 1) >= rD) --fR;
-      sL = fL;
-      sR = fR;
+      while (fL > 0 && cL >= lD) {
+        --fL;
+        cL = fL > 0 ? cut_at(fL - 1) : 0;
+      }
+      while (fR > 0 && cR >= rD) {
+        --fR;
+        cR = fR > 0 ? cut_at(fR - 1) : 0;
+      }
+      sL = __builtin_amdgcn_readfirstlane(fL);
+      sR = __builtin_amdgcn_readfirstlane(fR);
     } else {
       sL = 0;
       sR = 0;
@@ -332,29 +342,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       }
     }
 
-    // ---- online softmax over this block (log2 domain) ----
+    // ---- online softmax over this block (log2 domain).  The running max m_i
+    //      (per head) is refreshed, and O and l rescaled, only when some
+    //      head's max grows by more than 8, so every probability stays below
+    //      2^8; O / l and the partial (m, l) pairs are unaffected. ----
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
-    l_i *= alpha;
+    const float m_cand = mx * sl2;
+    if (__any(m_cand > m_i + 8.f)) {
+      const float m_new = fmaxf(m_i, m_cand);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+      l_i *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[db] *= alpha;
+      m_i = m_use;
+    }
     float e[8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        e[4 * blk + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], sl2, -m_use));
+        e[4 * blk + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], sl2, -m_i));
         l_i += e[4 * blk + r];
       }
     u32x4 pb;
 #pragma unroll
     for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) o[db] *= alpha;
-    m_i = m_new;
 
     // the V^T tile was written by other lanes of this wave
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

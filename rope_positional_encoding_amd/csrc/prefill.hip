@@ -201,8 +201,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   // carried from tile to tile.  A wave meets its key tiles in ascending
   // order, so the tile distances, and with them splitL and splitR, only
   // decrease; a few table reads per tile replace a 2 x 64-step scan.
+  // cL / cR hold the cutoff of group fL - 1 / fR - 1 in scalar registers,
+  // so a tile whose split points do not move reads no LDS.
   __shared__ int s_cut[FINE ? NG : 1];
   int fL = NG, fR = NG;
+  int cL = 0, cR = 0;
   if constexpr (FINE) {
     if (tid < NG) s_cut[tid] = a.cut[tid];
   }
@@ -211,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (FINE) cL = cR = cut_at(NG - 1);
 
   for (int it = 0; it < nk; ++it) {
     const int j0 = it * kTileKeys;
@@ -226,10 +230,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       // cutoffs are non-decreasing: splitL / splitR = 1 + last group below
       int sL = 0, sR = 0;
       if constexpr (FINE) {
-        while (fL > 0 && cut_at(fL - 1) >= lD) --fL;
-        while (fR > 0 && cut_at(fR - 1) >= rD) --fR;
-        sL = fL;
-        sR = fR;
+        while (fL > 0 && cL >= lD) {
+          --fL;
+          cL = fL > 0 ? cut_at(fL - 1) : 0;
+        }
+        while (fR > 0 && cR >= rD) {
+          --fR;
+          cR = fR > 0 ? cut_at(fR - 1) : 0;
+        }
+        sL = __builtin_amdgcn_readfirstlane(fL);
+        sR = __builtin_amdgcn_readfirstlane(fR);
       } else {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
