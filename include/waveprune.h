@@ -222,8 +222,9 @@ size_t wp_prefill_backward_workspace_size(int32_t B, int32_t n, int32_t Hq);
  * The key blocks are dealt to num_splits splits (0 = automatic, see
  * wp_decode_num_splits; at most one split per key block): split s takes
  * blocks s, s + S, s + 2S, ...  Splits are computed independently, then
- * merged.  Up to 16 query heads of a kv head are computed together; more
- * (Hq / Hkv > 16) run in passes of 16, each reading the cache again.
+ * merged.  Up to 32 query heads of a kv head are computed together, in one
+ * pass over the cache; more (Hq / Hkv > 32) run in passes of 32, each
+ * reading the cache again.
  * workspace: device memory of at least wp_decode_workspace_size(...) bytes,
  * 256-byte aligned, used for the per-split partial results.
  * counters (WP_FLAG_COUNT): device int64[3*(d_h/G)+1], as in wp_prefill but

@@ -458,13 +458,13 @@ wp_status decode_impl(const void* q, const void* k, const void* v_cache, void* o
   const long long blocks = (long long)B * Hkv * S;
   if (blocks > 2147483647LL || (long long)B * Hq > 2147483647LL)
     return fail(WP_ERR_SHAPE, "grid too large");
-  // The kernel holds at most 16 query heads of a kv head as MFMA columns.
-  // More heads per kv head run in passes of 16 (each pass reads the cache
-  // again; tile counts are taken in the first pass only); the passes share
-  // the workspace in stream order.
-  for (int h0 = 0; h0 < a.rs; h0 += 16) {
+  // The kernel holds at most 32 query heads of a kv head as MFMA columns
+  // (two sets of 16 sharing each K / V operand).  More heads per kv head run
+  // in passes of 32 (each pass reads the cache again; tile counts are taken
+  // in the first pass only); the passes share the workspace in stream order.
+  for (int h0 = 0; h0 < a.rs; h0 += 32) {
     wp::DecodeArgs p = a;
-    p.r = a.rs - h0 < 16 ? a.rs - h0 : 16;
+    p.r = a.rs - h0 < 32 ? a.rs - h0 : 32;
     p.Hq = Hkv * p.r;
     p.q = a.q + (int64_t)h0 * a.qs_h;
     p.o = a.o + (int64_t)h0 * a.os_h;

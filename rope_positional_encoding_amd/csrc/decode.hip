@@ -57,7 +57,10 @@ __device__ inline int mod_small(int j, int c, float rc) {
   return r;
 }
 
-template <int D, int G, bool COUNT, bool COMPACT>
+// HS head sets of 16: a launch takes up to 16 * HS query heads per kv head,
+// the MFMA columns of set hs being heads 16 hs .. 16 hs + 15; the K and V
+// operands of a block serve every set.
+template <int D, int G, bool COUNT, bool COMPACT, int HS>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
   constexpr int NP = D / 32;          // 32-dim MFMA steps of QK
   constexpr int NG = D / G;           // groups
@@ -71,6 +74,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   __shared__ __attribute__((aligned(16))) bf16 sV[kWaves][D * VS];
   __shared__ float sM[kWaves][16];
   __shared__ float sL[kWaves][16];
+  static_assert(HS == 1 || HS == 2, "head sets");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -87,15 +91,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   const int L = __builtin_amdgcn_readfirstlane(min(a.cache_len[b], a.Lmax));
   const int qp = __builtin_amdgcn_readfirstlane(a.q_pos[b]);
 
-  // Q^T operand: column n16 = head kvh*r + n16 (zero beyond r), dims
-  // [32p + 8q4, 32p + 8q4 + 8) of step p.
-  u32x4 qr[NP];
-  {
+  // Q^T operand of head set hs: column n16 = head kvh*rs + 16hs + n16 (zero
+  // from r on), dims [32p + 8q4, 32p + 8q4 + 8) of step p.
+  u32x4 qr[HS][NP];
+#pragma unroll
+  for (int hs = 0; hs < HS; ++hs) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bf16* qb = a.q + (int64_t)b * a.qs_b + (int64_t)(kvh * a.rs + n16) * a.qs_h + q4 * 8;
+    const int hd = 16 * hs + n16;
+    const bf16* qb = a.q + (int64_t)b * a.qs_b + (int64_t)(kvh * a.rs + hd) * a.qs_h + q4 * 8;
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      qr[p] = (n16 < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
+      qr[hs][p] = (hd < a.r) ? *reinterpret_cast<const u32x4*>(qb + p * 32) : zero;
   }
 
   // K / V of this (sequence, kv head) through raw buffer resources.  For the
@@ -130,10 +136,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   constexpr int kOut = 0x7ffffff0;    // any offset >= the resource size
 
   bf16* sv = sV[wave];
-  float m_i = -INFINITY, l_i = 0.f;
-  f32x4 o[ND];
+  float m_i[HS], l_i[HS];
+  f32x4 o[HS][ND];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hs = 0; hs < HS; ++hs) {
+    m_i[hs] = -INFINITY;
+    l_i[hs] = 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) o[hs][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Tile-class counters: per group in registers for coarse groups; for fine
   // groups (up to 64) a workgroup histogram of splitL / splitR in LDS,
@@ -260,11 +271,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // ---- S^T = K Q^T per 16-key block, group by group ----
-    f32x4 s[2];
+    // ---- S^T = K Q^T per 16-key block and head set, group by group ----
+    f32x4 s[HS][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) s[hs][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int g_lo = (32 * p) / G;             // groups covered by step p
@@ -274,14 +286,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
         // group of operand word w (dims 32p + 8q4 + 2w, +1)
         auto grp = [&](int w) { return (32 * p + 8 * q4 + 2 * w) / G; };
         if (g_lo >= sR) {                          // all full: skipped lanes read zero
-          s[blk] = mfma16(R.k[blk][p], qr[p], s[blk]);
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) s[hs][blk] = mfma16(R.k[blk][p], qr[hs][p], s[hs][blk]);
           continue;
         }
         const bool any_full = g_hi >= sR;          // the step's last group is full
         if (any_full) {
           const u32x4 op = FINE ? keep_words(R.k[blk][p], [&](int w) { return grp(w) >= sR; })
                                 : ((g >= sR) ? R.k[blk][p] : zero);
-          s[blk] = mfma16(op, qr[p], s[blk]);
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs) s[hs][blk] = mfma16(op, qr[hs][p], s[hs][blk]);
         }
         if constexpr (FINE) {
           // a runtime loop over just this step's partial groups: unrolled
@@ -290,12 +304,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll 1
           for (int gg = max(g_lo, sL); gg < min(g_hi + 1, sR); ++gg) {
             const u32x4 op = keep_words(R.k[blk][p], [&](int w) { return grp(w) == gg; });
-            const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
             const int cg = __builtin_amdgcn_readfirstlane(s_cut[gg]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = jb + 16 * blk + 4 * q4 + r;
-              s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+            for (int hs = 0; hs < HS; ++hs) {
+              const f32x4 t = mfma16(op, qr[hs][p], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int j = jb + 16 * blk + 4 * q4 + r;
+                s[hs][blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+              }
             }
           }
         } else {
@@ -303,12 +320,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
           for (int gg = g_lo; gg <= g_hi; ++gg) {
             if (gg < sL || gg >= sR) continue;     // only partial groups
             const u32x4 op = (g == gg) ? R.k[blk][p] : zero;
-            const f32x4 t = mfma16(op, qr[p], f32x4{0.f, 0.f, 0.f, 0.f});
             const int cg = a.cut[gg];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = jb + 16 * blk + 4 * q4 + r;
-              s[blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+            for (int hs = 0; hs < HS; ++hs) {
+              const f32x4 t = mfma16(op, qr[hs][p], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int j = jb + 16 * blk + 4 * q4 + r;
+                s[hs][blk][r] += (qp - j <= cg) ? t[r] : 0.f;
+              }
             }
           }
         }
@@ -317,7 +337,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = jb + 16 * blk + 4 * q4 + r;
-          if (j > jb1) s[blk][r] = -INFINITY;
+#pragma unroll
+          for (int hs = 0; hs < HS; ++hs)
+            if (j > jb1) s[hs][blk][r] = -INFINITY;
         }
       }
     }
@@ -346,31 +368,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     //      (per head) is refreshed, and O and l rescaled, only when some
     //      head's max grows by more than 8, so every probability stays below
     //      2^8; O / l and the partial (m, l) pairs are unaffected. ----
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_cand = mx * sl2;
-    if (__any(m_cand > m_i + 8.f)) {
-      const float m_new = fmaxf(m_i, m_cand);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
-      l_i *= alpha;
+    u32x4 pb[HS];
 #pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      m_i = m_use;
-    }
-    float e[8];
+    for (int hs = 0; hs < HS; ++hs) {
+      const f32x4* sh = s[hs];
+      float mx = fmaxf(fmaxf(fmaxf(sh[0][0], sh[0][1]), fmaxf(sh[0][2], sh[0][3])),
+                       fmaxf(fmaxf(sh[1][0], sh[1][1]), fmaxf(sh[1][2], sh[1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_cand = mx * sl2;
+      if (__any(m_cand > m_i[hs] + 8.f)) {
+        const float m_new = fmaxf(m_i[hs], m_cand);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_i[hs] - m_use);
+        l_i[hs] *= alpha;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e[4 * blk + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], sl2, -m_i));
-        l_i += e[4 * blk + r];
+        for (int db = 0; db < ND; ++db) o[hs][db] *= alpha;
+        m_i[hs] = m_use;
       }
-    u32x4 pb;
+      float e[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[4 * blk + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[blk][r], sl2, -m_i[hs]));
+          l_i[hs] += e[4 * blk + r];
+        }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pb[hs][w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+    }
 
     // the V^T tile was written by other lanes of this wave
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -379,7 +405,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const u32x4 va = *reinterpret_cast<const u32x4*>(&sv[(16 * db + n16) * VS + 8 * q4]);
-      o[db] = mfma16(va, pb, o[db]);
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) o[hs][db] = mfma16(va, pb[hs], o[hs][db]);
     }
     // the next block overwrites the tile only after these reads completed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -400,44 +427,50 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
     compute_block(RA, jb);
   }
 
-  // ---- merge the 4 waves of this split through LDS ----
-  const float l_tot = l_i + __shfl_xor(l_i, 16);
-  const float l_all = l_tot + __shfl_xor(l_tot, 32);
-  if (q4 == 0) {
-    sM[wave][n16] = m_i;
-    sL[wave][n16] = l_all;
-  }
-  __syncthreads();   // every wave is done with its V^T tile: reuse LDS for O
+  // ---- merge the 4 waves of this split through LDS, one head set at a
+  //      time (the set's O tiles reuse the V^T tiles' LDS) ----
   float* sO = reinterpret_cast<float*>(&sV[0][0]);   // [kWaves][16][D]
   static_assert(sizeof(float) * kWaves * 16 * D <= sizeof(bf16) * kWaves * D * VS, "LDS reuse");
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sO[(wave * 16 + n16) * D + 16 * db + 4 * q4 + r] = o[db][r];
-  __syncthreads();
-
-  const int r_heads = a.r;
-  for (int idx = tid; idx < r_heads * D; idx += kThreads) {
-    const int hd = idx / D;
-    const int d = idx - hd * D;
-    float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sM[w][hd]);
-    float acc = 0.f, lsum = 0.f;
-    if (mm != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(sM[w][hd] - mm);
-        acc += sc * sO[(w * 16 + hd) * D + d];
-        lsum += sc * sL[w][hd];
-      }
+  for (int hs = 0; hs < HS; ++hs) {
+    const float l_tot = l_i[hs] + __shfl_xor(l_i[hs], 16);
+    const float l_all = l_tot + __shfl_xor(l_tot, 32);
+    // every wave is done with its V^T tile (first set) or with the previous
+    // set's merge reads before the LDS is written again
+    __syncthreads();
+    if (q4 == 0) {
+      sM[wave][n16] = m_i[hs];
+      sL[wave][n16] = l_all;
     }
-    const int h = kvh * a.r + hd;
-    const int64_t pi = ((int64_t)b * a.Hq + h) * a.S + split;
-    a.part_o[pi * D + d] = acc;
-    if (d == 0) {
-      a.part_ml[2 * pi] = mm;
-      a.part_ml[2 * pi + 1] = lsum;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sO[(wave * 16 + n16) * D + 16 * db + 4 * q4 + r] = o[hs][db][r];
+    __syncthreads();
+
+    const int r_set = min(16, a.r - 16 * hs);     // heads of this set in the launch
+    for (int idx = tid; idx < r_set * D; idx += kThreads) {
+      const int hd = idx / D;
+      const int d = idx - hd * D;
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sM[w][hd]);
+      float acc = 0.f, lsum = 0.f;
+      if (mm != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float sc = __builtin_amdgcn_exp2f(sM[w][hd] - mm);
+          acc += sc * sO[(w * 16 + hd) * D + d];
+          lsum += sc * sL[w][hd];
+        }
+      }
+      const int h = kvh * a.r + 16 * hs + hd;
+      const int64_t pi = ((int64_t)b * a.Hq + h) * a.S + split;
+      a.part_o[pi * D + d] = acc;
+      if (d == 0) {
+        a.part_ml[2 * pi] = mm;
+        a.part_ml[2 * pi + 1] = lsum;
+      }
     }
   }
 
@@ -501,18 +534,24 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int e = 0; e < PER; ++e) op[lane + 64 * e] = static_cast<__bf16>(acc[e] * inv);
 }
 
-template <int D, int G, bool COMPACT>
-hipError_t launch_dg(const DecodeArgs& a, bool count, hipStream_t s) {
+template <int D, int G, bool COMPACT, int HS>
+hipError_t launch_dgh(const DecodeArgs& a, bool count, hipStream_t s) {
   const long long blocks = (long long)a.B * a.Hkv * a.S;
   if (blocks <= 0) return hipSuccess;
   if (count)
-    hipLaunchKernelGGL((decode_split_kernel<D, G, true, COMPACT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, true, COMPACT, HS>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, false, COMPACT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, false, COMPACT, HS>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+// one head set for up to 16 query heads per kv head, two for up to 32
+template <int D, int G, bool COMPACT>
+hipError_t launch_dg(const DecodeArgs& a, bool count, hipStream_t s) {
+  return a.r > 16 ? launch_dgh<D, G, COMPACT, 2>(a, count, s) : launch_dgh<D, G, COMPACT, 1>(a, count, s);
 }
 
 template <int D, int G>

@@ -75,7 +75,7 @@ struct DecodeArgs {
   int64_t vs_b, vs_t, vs_h;
   int64_t os_b, os_h;
   int B, Lmax, Hq, Hkv;
-  int r;          // query heads of each kv head in this launch (<= 16)
+  int r;          // query heads of each kv head in this launch (<= 32)
   int rs;         // query-head index stride between kv heads (the model's Hq / Hkv)
   int S;          // splits; split s takes key blocks s, s + S, s + 2S, ...
   float scale_log2;

@@ -75,7 +75,7 @@ hipError_t launch_prefill16(const PrefillArgs& a, bool count, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int d_h, int G, bool count, hipStream_t) {
-  if (a.r < 1 || a.r > 16 || a.S < 1) return hipErrorInvalidValue;
+  if (a.r < 1 || a.r > 32 || a.S < 1) return hipErrorInvalidValue;
   for (int b = 0; b < a.B; ++b) {
     touch(a.cache_len, 4 * b, 4 * b + 3);
     touch(a.q_pos, 4 * b, 4 * b + 3);

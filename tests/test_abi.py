@@ -295,8 +295,8 @@ def test_decode_cache_span_limits():
 def test_decode_validation_codes():
     assert _decode(ws=None) == -1
     assert _decode(d_h=80) == -3
-    # more than 16 query heads per kv head are accepted (they run in passes of
-    # 16): validation stops at the small workspace
+    # more than 32 query heads per kv head are accepted (they run in passes of
+    # 32): validation stops at the small workspace
     assert _decode(Hq=64, Hkv=2, ws_bytes=16) == -5
     assert _decode(ws_bytes=16) == -5
     assert _decode(ws=ctypes.c_void_p(0x7F0000000010)) == -4

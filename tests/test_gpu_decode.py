@@ -186,17 +186,21 @@ def test_decode_strided_views():
 
 # B, Lmax, Hq, Hkv, d, G, theta, cache lengths, splits
 WIDE_GQA = [
-    (2, 900, 32, 1, 128, 16, 1e3, [900, 451], 0),      # 32 query heads on one kv head: two passes
-    (1, 1500, 40, 2, 64, 32, 300.0, [1500], 3),         # 20 per kv head: passes of 16 and 4
+    (2, 900, 32, 1, 128, 16, 1e3, [900, 451], 0),      # 32 query heads on one kv head: two head sets
+    (1, 1500, 40, 2, 64, 32, 300.0, [1500], 3),         # 20 per kv head: sets of 16 and 4
     (2, 700, 48, 2, 128, 2, 1e4, [700, 1], 0),          # 24 per kv head, exact rule
+    (1, 600, 64, 1, 128, 16, 1e3, [600], 0),            # 64 per kv head: two passes of 32
+    (1, 700, 80, 2, 64, 32, 1e4, [700], 2),             # 40 per kv head: passes of 32 and 8
+    (2, 500, 17, 1, 128, 4, 300.0, [500, 33], 0),       # 17: the second set holds one head
 ]
 
 
 @pytest.mark.parametrize("B,Lmax,Hq,Hkv,d,G,theta,lens,splits", WIDE_GQA)
 def test_decode_wide_gqa(B, Lmax, Hq, Hkv, d, G, theta, lens, splits):
-    """More than 16 query heads per kv head (MQA-style): the heads run in
-    passes of 16 over the same cache; every head against the oracle and the
-    tile counters counted once per (sequence, kv head, key block)."""
+    """More than 16 query heads per kv head (MQA-style): up to 32 heads share
+    one pass over the cache as two MFMA head sets, more run in passes of 32;
+    every head against the oracle and the tile counters counted once per
+    (sequence, kv head, key block)."""
     say("decode wide GQA: B=%d Lmax=%d Hq=%d Hkv=%d d=%d G=%d lens=%s" % (B, Lmax, Hq, Hkv, d, G, lens))
     q = synth.normal_bits(47, 0, B, (Hq, d))
     kc = synth.normal_bits(47, 1, B * Lmax, (Hkv, d))
