@@ -17,8 +17,9 @@
 //    online-softmax state for the GQA heads.
 //  * QK on v_mfma_f32_16x16x32_bf16 with the keys as rows: each lane loads
 //    16 contiguous bytes of one key row straight from HBM into the MFMA A
-//    operand; the GQA heads (<= 16) are the B columns, held in registers.
-//    Lanes whose 8 dims belong to a skipped group issue no load.
+//    operand; the GQA heads are the B columns, held in registers: up to 16,
+//    or up to 32 as two head sets that share every K and V operand.  Lanes
+//    whose 8 dims belong to a skipped group issue no load.
 //  * P.V on the same MFMA as O^T = V^T P^T: the probabilities are already in
 //    the B layout; V is staged through a per-wave LDS tile written transposed
 //    (keys permuted to match), so the A operand is one 16-byte LDS read.
