@@ -28,6 +28,12 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source options.  The prefill kernel is scheduled with LLVM's max-ILP
+# strategy (AMDGPU machine scheduler): same instructions, about 1% faster at
+# 32K than the default occupancy-first strategy, no spills (the occupancy is
+# fixed at two waves per SIMD by the register budget anyway).
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
 
 def _run(cmd, verbose):
     if verbose:
@@ -49,7 +55,7 @@ def build(verbose: bool = False, extra=()) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
