@@ -126,8 +126,8 @@ def measured_traffic(kernel):
 
 # ---------------------------------------------------------------------------
 def _oracle_threads():
-    """Host threads for the oracle: the CPUs this process may run on (at
-    most 16, the host share of one GPU on the box)."""
+    """Host threads for the oracle: the CPUs this process may run on, at
+    most 16 (a host share of 16 threads per GPU)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -527,7 +527,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the path needs no "
+        print("bench.py: measures one GPU only (the path needs no "
               "collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
