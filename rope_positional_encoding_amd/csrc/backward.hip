@@ -237,15 +237,23 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     for (int c = 0; c < NCH; ++c) br[c] = (j < n) ? *reinterpret_cast<const u32x4*>(p + c * 16) : zero;
   }
 
-  // DMA: load i of this lane fills chunk p = wave*64 + lane + i*512 of a
-  // stage ([Q | dO], TCH chunks each): tile row pt / CPR, logical chunk
-  // (pt % CPR) ^ dual_swz(row), pt = p % TCH
+  // DMA: load i of an issuing lane fills chunk p of a stage ([Q | dO], TCH
+  // chunks each): tile row pt / CPR, logical chunk (pt % CPR) ^
+  // dual_swz(row), pt = p % TCH.  Coarse groups: only the first waves issue
+  // it, p = wave*64 + lane + 256*i (2 NL loads per lane): the second waves
+  // set the pace of a step and the first waves wait for them at the barrier
+  // anyway (10% faster at 32K, G = 16).  Fine groups keep the first waves
+  // busier with their per-group loops, so all eight waves share the DMA
+  // there, p = wave*64 + lane + 512*i.
   const int qrow_b = (int)(a.qs_t * 2);
   const int grow_b = (int)(a.gs_t * 2);
-  int doff[NL];
+  constexpr bool DMA1 = !FINE;                  // DMA by the first waves only
+  constexpr int NLD = DMA1 ? 2 * NL : NL;       // DMA loads per issuing lane and tile
+  constexpr int DSTRIDE = DMA1 ? 256 : kKvThreads;
+  int doff[NLD];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int p = wave * 64 + lane + kKvThreads * i;
+  for (int i = 0; i < NLD; ++i) {
+    const int p = (DMA1 ? (wave & 3) : wave) * 64 + lane + DSTRIDE * i;
     const int pt = p % TCH;
     const int row = pt / CPR;
     doff[i] = row * (p < TCH ? qrow_b : grow_b) + ((pt % CPR) ^ dual_swz<D>(row)) * 16;
@@ -268,8 +276,8 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
     const __amdgpu_buffer_rsrc_t grs = uniform_rsrc(
         a.dout + (int64_t)b * a.gs_b + (int64_t)i0 * a.gs_t + (int64_t)h * a.gs_h, (rows - 1) * grow_b + 2 * D);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int p0 = wave * 64 + kKvThreads * i;  // wave-uniform: Q or dO
+    for (int i = 0; i < NLD; ++i) {
+      const int p0 = wave * 64 + DSTRIDE * i;  // wave-uniform: Q or dO
       dma16(p0 < TCH ? qrs : grs, dst + p0 * 16, doff[i]);
     }
     if (wave == 0 && lane < 16)
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
                   const unsigned char* __restrict__ sg, const float* __restrict__ sl, float* __restrict__ pb,
                   unsigned char* __restrict__ dst, float* __restrict__ ldst) {
     constexpr bool PW = decltype(role)::first;
-    if (u + kPrefetch < total) load_tile(lhr, lti, dst, ldst);
+    if ((!DMA1 || PW) && u + kPrefetch < total) load_tile(lhr, lti, dst, ldst);
     const int v = PW ? u : u - 1;
     const int i0 = __builtin_amdgcn_readfirstlane((t0 + cti) * 32);
     const int i1 = min(n, i0 + 32) - 1;
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
   // tiles 0 .. kPrefetch-1 into stages 0 .. kPrefetch-1
 #pragma unroll
   for (int t = 0; t < kPrefetch; ++t)
-    if (t < total) load_tile(t / nt, t % nt, &smem[t][0], &s_ld[t][0]);
+    if ((!DMA1 || pwave) && t < total) load_tile(t / nt, t % nt, &smem[t][0], &s_ld[t][0]);
   wait_vm<0>();
   bare_barrier();
 
@@ -550,12 +558,12 @@ __global__ __launch_bounds__(kKvThreads) void bwd_dkdv_kernel(BackwardArgs a) {
       // tile u + 1 must have landed (later tiles may still be in flight)
       // and every wave be done with this step's stages
       const int ahead = min(total - 1, u + kPrefetch) - (u + 1);   // tiles issued after u + 1
-      if (ahead <= 0) {
+      if (ahead <= 0 || (DMA1 && !PW)) {
         wait_vm<0>();
       } else if (wave == 0) {
-        if (ahead == 1) wait_vm<NL + 1>(); else wait_vm<2 * (NL + 1)>();
+        if (ahead == 1) wait_vm<NLD + 1>(); else wait_vm<2 * (NLD + 1)>();
       } else {
-        if (ahead == 1) wait_vm<NL>(); else wait_vm<2 * NL>();
+        if (ahead == 1) wait_vm<NLD>(); else wait_vm<2 * NLD>();
       }
       bare_barrier();
     }
