@@ -349,10 +349,13 @@ def oracle_decode_rate(dq, kc, vc, L, q_pos, cut, G, threads):
     return dt, 2.0 * 2 * B * L * kc.shape[2] * kc.shape[3]
 
 
-def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops):
+def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops, alg_fwd_flops):
     """wp_prefill_backward at the prefill shape: 1 warmup, median of 3, for
     the WavePrune table and the dense baseline.  Dense-equivalent work: five
-    d_h-long products per causal pair (S, dP, dV, dK, dQ) = 2.5x the forward."""
+    d_h-long products per causal pair (S, dP, dV, dK, dQ) = 2.5x the forward.
+    Algorithmic work: dP and dV over all d_h dims, S, dK and dQ over the kept
+    groups only, i.e. 2 x (the forward's P.V part) + 3 x (its kept-group QK
+    part); the roofline fraction is taken on it, as for the forward."""
     import torch
     log("bench: prefill backward")
     o, lse = W.prefill(q, k, v, cut, G, return_lse=True)
@@ -374,9 +377,16 @@ def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops):
             ts.append(e0.elapsed_time(e1))
         res["dense" if dense else "wp"] = statistics.median(ts)
     bwd_flops = 2.5 * dense_fwd_flops
+    pv = dense_fwd_flops / 2.0                    # the forward's P.V products (all dims)
+    bwd_alg = 2.0 * pv + 3.0 * (alg_fwd_flops - pv)
+    alg_tflops = bwd_alg / (res["wp"] * 1e-3) / 1e12
     return {"ms_median": round(res["wp"], 3), "dense_ms_median": round(res["dense"], 3),
             "dense_equiv_tflops": round(bwd_flops / (res["wp"] * 1e-3) / 1e12, 2),
+            "algorithmic_tflops": round(alg_tflops, 2),
+            "algorithmic_fraction_of_dense": round(bwd_alg / bwd_flops, 4),
+            "frac_of_peak": round(alg_tflops / PEAK_BF16_TFLOPS, 4),
             "dense_tflops": round(bwd_flops / (res["dense"] * 1e-3) / 1e12, 2),
+            "dense_frac_of_peak": round(bwd_flops / (res["dense"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "speedup_vs_dense": round(res["dense"] / res["wp"], 4)}
 
 
@@ -693,7 +703,7 @@ def main():
                               "avg_ms": round(davg, 4)}
     bwd_ms = None
     if not args.no_backward:
-        out["prefill_backward"] = bench_backward(W, qr, kr, v, cut, G, n, Hq, d, dense_f)
+        out["prefill_backward"] = bench_backward(W, qr, kr, v, cut, G, n, Hq, d, dense_f, alg_f)
         bwd_ms = out["prefill_backward"]["ms_median"]
     if not args.no_kcache:
         out["decode_kcache"] = bench_kcache(W, dqr[:, 0], kcs, vcs, cl, qp, cut, G, ws, od, dec_alg, dmed)
