@@ -708,15 +708,17 @@ __global__ __launch_bounds__(kDqThreads, G == 2 ? 1 : 2) void bwd_dq_kernel(Back
   };
   // row-wise reads of rows 32kb + l32 (the swizzles of rows 32kb + l32 do not
   // depend on kb)
-  int kread[NCH], vread[NCH];
+  // The offset of step c is l32*RB + ((2c + hh) ^ sw) * 16; the swizzle sw
+  // has at most 4 bits and the row offset starts at bit 7, so it equals
+  // (l32*RB + ((hh ^ sw) & 1) * 16 + (sw >> 1) * 32) ^ (c << 5): one base
+  // register per operand instead of one per step (the per-step arrays
+  // spilled at d_h = 128, and every reload waited for the DMA in flight).
+  int kbase_off, vbase_off;
   {
     const int swk = dual_swz<D>(l32);
     const int swv = (l32 / KRB) & (CPR - 1);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      kread[c] = l32 * RB + ((2 * c + hh) ^ swk) * 16;
-      vread[c] = l32 * RB + ((2 * c + hh) ^ swv) * 16;
-    }
+    kbase_off = l32 * RB + ((hh ^ swk) & 1) * 16 + (swk >> 1) * 32;
+    vbase_off = l32 * RB + ((hh ^ swv) & 1) * 16 + (swv >> 1) * 32;
   }
   // transposing reads of K (rows 16kc + 4hh + e4 and + 8)
   const int grp = lane >> 4;
@@ -762,8 +764,16 @@ __global__ __launch_bounds__(kDqThreads, G == 2 ? 1 : 2) void bwd_dq_kernel(Back
       } else {
         split_points<NG>(a.cut, max(0, i0w - j1), i1w - j0, sL, sR);
       }
-      auto kop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + kread[c]); };
-      auto vop = [&](int kb, int c) { return *reinterpret_cast<const u32x4*>(sv + kb * 32 * RB + vread[c]); };
+      // the bases are re-declared live here each tile, so that the compiler
+      // forms the per-step offsets at their use instead of hoisting eight of
+      // each out of the loop
+      asm volatile("" : "+v"(kbase_off), "+v"(vbase_off));
+      auto kop = [&](int kb, int c) {
+        return *reinterpret_cast<const u32x4*>(sk + kb * 32 * RB + (kbase_off ^ (c << 5)));
+      };
+      auto vop = [&](int kb, int c) {
+        return *reinterpret_cast<const u32x4*>(sv + kb * 32 * RB + (vbase_off ^ (c << 5)));
+      };
       const int base = qi - j0;                    // distance = base - (32kb + out_row(r))
 
       u32x4 dsp[4];                                // dS^T as B operands, 16 keys each
