@@ -1,8 +1,9 @@
-"""Seeded random shapes for prefill and decode against the oracle, all rows:
-n, cache lengths, GQA ratio, d_h, G (including the fine groups), theta
-(log-uniform, so skip / partial / full all occur at these lengths) and the
-dense flag drawn per case from a fixed seed.  Gate: max-abs 2e-2, mean-abs
-2e-3 on O; tile counters bit-exact."""
+"""Seeded random shapes for prefill, decode and the prefill backward against
+the oracle, all rows: n, cache lengths, GQA ratio, d_h, G (including the fine
+groups), theta (log-uniform, so skip / partial / full all occur at these
+lengths) and the dense flag drawn per case from a fixed seed.  Gate: max-abs
+2e-2, mean-abs 2e-3 on O, tile counters bit-exact; gradients within the
+element-wise bound of tests/bwd_bound.py (as in tests/test_gpu_backward.py)."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +11,7 @@ import torch
 import oracle as O
 import rope_positional_encoding_amd as W
 from rope_positional_encoding_amd import synth
+import bwd_bound as BB
 from gpu_util import bf16_to_np, bits_to_dev, compare, dev, say, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +91,24 @@ def test_decode_random_shape(i):
         c, vis = O.decode_tile_counts(q_pos[b], lens[b], W.decode_tiling(d, G), table)
         exp += (np.concatenate([c.ravel(), [vis]]) * Hkv).astype(np.int64)
     assert np.array_equal(cnt.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_backward_random_shape(i):
+    d, G, Hkv, Hq, theta, dense, rng = _case(200 + i)
+    n = int(rng.integers(1, 400))
+    say("backward random %d: n=%d Hq=%d Hkv=%d d=%d G=%d theta=%.4g dense=%s" % (i, n, Hq, Hkv, d, G, theta, dense))
+    x = [synth.normal_bits(500 + i, t, n, (h, d)) for t, h in ((0, Hq), (1, Hkv), (2, Hkv), (3, Hq))]
+    qt, kt, vt, gt = (bits_to_dev(a, (1, n, a.shape[1], d)) for a in x)
+    cut = W.group_cutoffs(theta, d, G)
+    o, lse = W.prefill(qt, kt, vt, None if dense else cut, G, dense=dense, return_lse=True)
+    grads = W.prefill_backward(qt, kt, vt, o, gt, lse, None if dense else cut, G, dense=dense)
+    torch.cuda.synchronize()
+    x64 = [to_f64(a) for a in x]
+    dim_cut = _dim_cut(theta, d, G, dense)
+    ref = O.prefill_backward(*x64, dim_cut)
+    R = BB.backward_terms(*x64, dim_cut)
+    for name, gg, rr, RR in zip(("dQ", "dK", "dV"), grads, ref, R):
+        got = bf16_to_np(gg).reshape(rr.shape)
+        BB.check(got, rr, RR, "backward random %d %s" % (i, name), say)
+        assert np.abs(got - rr).mean() <= 2e-3, name
