@@ -63,6 +63,16 @@ def prefill_flops(n, Hq, B, d_h, G, cut):
     return dense * k, alg * k, exe * k
 
 
+def backward_flops(dense_fwd_flops, alg_fwd_flops):
+    """Dense-equivalent and algorithmic FLOPs of the prefill backward from the
+    forward's: five d_h-long products per causal pair (S, dP, dV, dK, dQ) =
+    2.5x the dense forward; algorithmically dP and dV cover every dim while
+    S, dK and dQ cover the kept groups only, i.e. 2 x the forward's P.V part
+    (half its dense work) + 3 x its kept-group QK part."""
+    pv = dense_fwd_flops / 2.0
+    return 2.5 * dense_fwd_flops, 2.0 * pv + 3.0 * (alg_fwd_flops - pv)
+
+
 def decode_bytes(L, q_pos, Hkv, Hq, B, d_h, G, cut):
     """Dense KV bytes, algorithmic bytes (kept K groups + all V + q/o) and
     the bytes of the K/V reads the kernel issues (per 32-key block)."""
@@ -376,9 +386,7 @@ def bench_backward(W, q, k, v, cut, G, n, Hq, d, dense_fwd_flops, alg_fwd_flops)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         res["dense" if dense else "wp"] = statistics.median(ts)
-    bwd_flops = 2.5 * dense_fwd_flops
-    pv = dense_fwd_flops / 2.0                    # the forward's P.V products (all dims)
-    bwd_alg = 2.0 * pv + 3.0 * (alg_fwd_flops - pv)
+    bwd_flops, bwd_alg = backward_flops(dense_fwd_flops, alg_fwd_flops)
     alg_tflops = bwd_alg / (res["wp"] * 1e-3) / 1e12
     return {"ms_median": round(res["wp"], 3), "dense_ms_median": round(res["dense"], 3),
             "dense_equiv_tflops": round(bwd_flops / (res["wp"] * 1e-3) / 1e12, 2),
