@@ -13,7 +13,7 @@ import torch
 import oracle as O
 from rope_positional_encoding_amd import synth
 
-# spec bar for bf16-in / fp32-accumulate O on N(0,1) V
+# parity gate for bf16-in / fp32-accumulate O on N(0,1) V (max-abs, mean-abs)
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 
